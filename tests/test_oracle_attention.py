@@ -1,0 +1,190 @@
+"""Pins for the oracle's attention: a 50-digit mpmath brute force over the
+whole decode step (dequantization re-derived here from the raw bytes), a
+closed-form two-token case, and the softmax invariants (weights sum to one,
+identical keys give the mean of V, one token gives that token's V, zero
+scale gives the mean, a dominant key selects its V, causal rows equal a
+truncated context, token order does not matter)."""
+import math
+
+import mpmath
+import numpy as np
+import pytest
+
+from oracle import kvq_oracle as O
+
+mpmath.mp.dps = 50
+
+
+def _half_mp(bits: int):
+    s = -1 if bits & 0x8000 else 1
+    e = (bits >> 10) & 0x1F
+    f = bits & 0x3FF
+    if e == 0:
+        return s * mpmath.mpf(f) * mpmath.mpf(2) ** -24
+    return s * mpmath.mpf(1024 + f) * mpmath.mpf(2) ** (e - 25)
+
+
+def _signed8(b: int) -> int:
+    return b - 256 if b >= 128 else b
+
+
+def _k_row_mp(words, dbits):
+    """dequantized K row from raw words: byte k of word w is element 4w+k."""
+    vals = []
+    for w in words:
+        for k in range(4):
+            vals.append(_signed8((int(w) >> (8 * k)) & 0xFF))
+    return [mpmath.mpf(v) * _half_mp(int(dbits[i // 32])) for i, v in enumerate(vals)]
+
+
+def _v_row_mp(payload, dbits, fmt, D):
+    out = [None] * D
+    if fmt == O.V_Q4_0:
+        for b in range(D // 32):
+            d = _half_mp(int(dbits[b]))
+            for j in range(16):
+                byte = int(payload[16 * b + j])
+                out[32 * b + j] = (mpmath.mpf(byte & 15) - 8) * d
+                out[32 * b + j + 16] = (mpmath.mpf(byte >> 4) - 8) * d
+    else:
+        for i in range(D):
+            out[i] = mpmath.mpf(_signed8(int(payload[i]))) * _half_mp(int(dbits[i // 32]))
+    return out
+
+
+def _q_row_mp(codes, d):
+    return [mpmath.mpf(int(c)) * mpmath.mpf(float(d[i // 32])) for i, c in enumerate(codes)]
+
+
+def _mp_attention(q_row, k_rows, v_rows, scale):
+    s = [scale * mpmath.fsum(a * b for a, b in zip(q_row, kr)) for kr in k_rows]
+    m = max(s)
+    e = [mpmath.exp(x - m) for x in s]
+    z = mpmath.fsum(e)
+    D = len(v_rows[0])
+    return [mpmath.fsum(e[t] * v_rows[t][c] for t in range(len(e))) / z for c in range(D)]
+
+
+@pytest.mark.parametrize("fmt", [O.V_Q4_0, O.V_Q8_0])
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_attention_mp_bruteforce(fmt, causal):
+    rng = np.random.default_rng(10 + fmt + 2 * causal)
+    S, Tq, Hq, Hkv, D, Lmax = 2, 2, 4, 2, 32, 8
+    seq_len = [8, 5]
+    q = rng.standard_normal((S, Tq, Hq, D)).astype(np.float32)
+    k = (rng.standard_normal((S, Hkv, Lmax, D)) * 2).astype(np.float32)
+    v = rng.standard_normal((S, Hkv, Lmax, D)).astype(np.float32)
+    kw, kd = O.encode_k(k)
+    vp, vd = O.encode_v(v, fmt)
+    scale = 1 / math.sqrt(D)
+    got = O.decode_attention(q, kw, kd, vp, vd, fmt, seq_len, scale, causal)
+    qc, qd = O.quantize_q(q)
+    G = Hq // Hkv
+    for i in range(S):
+        L = seq_len[i]
+        for j in range(Tq):
+            n_vis = L - Tq + j + 1 if causal else L
+            for h in range(Hq):
+                kvh = h // G
+                k_rows = [_k_row_mp(kw[i, kvh, t], kd[i, kvh, t]) for t in range(n_vis)]
+                v_rows = [_v_row_mp(vp[i, kvh, t], vd[i, kvh, t], fmt, D) for t in range(n_vis)]
+                want = _mp_attention(_q_row_mp(qc[i, j, h], qd[i, j, h]), k_rows, v_rows,
+                                     mpmath.mpf(scale))
+                want = np.array([float(x) for x in want])
+                np.testing.assert_allclose(got[i, j, h], want, rtol=1e-12, atol=1e-13)
+
+
+def test_closed_form_two_tokens():
+    # q = 127 e0 (d = 1), k0 = 0, k1 = 127 e0 (d = 1): scores 0 and
+    # 16129 * scale; with scale = ln 3 / 16129 the weights are 1/4 and 3/4.
+    D = 32
+    q = np.zeros((1, 1, 1, D), np.float32)
+    q[..., 0] = 127
+    k = np.zeros((1, 1, 2, D), np.float32)
+    k[0, 0, 1, 0] = 127
+    v = np.zeros((1, 1, 2, D), np.float32)
+    v[0, 0, 0, 0] = 127
+    v[0, 0, 1, 1] = -127
+    kw, kd = O.encode_k(k)
+    vp, vd = O.encode_v(v, O.V_Q8_0)
+    out = O.decode_attention(q, kw, kd, vp, vd, O.V_Q8_0, [2], math.log(3) / 16129, False)
+    want = np.zeros(D)
+    want[0] = 127 / 4
+    want[1] = -127 * 3 / 4
+    np.testing.assert_allclose(out[0, 0, 0], want, rtol=1e-13, atol=1e-12)
+
+
+def _rand(rng, *shape):
+    return rng.standard_normal(shape)
+
+
+def test_weights_sum_to_one_and_nonnegative():
+    rng = np.random.default_rng(20)
+    L = 24
+    qh, kh = _rand(rng, 3, 32), _rand(rng, L, 32) * 3
+    eye = np.eye(L, 32)                 # V = one-hot rows: output = the weights
+    w = O.softmax_attention(qh, kh, eye, 0.7, [L, L, 10])
+    assert np.all(w >= 0)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, atol=1e-12)
+    assert np.all(w[2, 10:] == 0)
+
+
+def test_identical_keys_give_mean_of_v():
+    rng = np.random.default_rng(21)
+    kh = np.repeat(_rand(rng, 1, 64), 17, axis=0)
+    vh = _rand(rng, 17, 64)
+    out = O.softmax_attention(_rand(rng, 2, 64), kh, vh, 1.3, [17, 17])
+    np.testing.assert_allclose(out, np.tile(vh.mean(axis=0), (2, 1)), rtol=1e-12, atol=1e-13)
+
+
+def test_single_token_zero_scale_dominant_key():
+    rng = np.random.default_rng(22)
+    qh, kh, vh = _rand(rng, 1, 32), _rand(rng, 9, 32), _rand(rng, 9, 32)
+    np.testing.assert_allclose(O.softmax_attention(qh, kh, vh, 0.5, [1])[0], vh[0], rtol=1e-14)
+    np.testing.assert_allclose(O.softmax_attention(qh, kh, vh, 0.0, [9])[0], vh.mean(axis=0),
+                               rtol=1e-12, atol=1e-13)
+    kd = kh.copy()
+    kd[4] = qh[0] * 100.0
+    np.testing.assert_allclose(O.softmax_attention(qh, kd, vh, 1.0, [9])[0], vh[4], rtol=1e-12)
+
+
+def test_causal_rows_equal_truncated_context_and_permutation():
+    rng = np.random.default_rng(23)
+    S, Tq, Hq, Hkv, D, L = 1, 4, 4, 1, 64, 40
+    q = rng.standard_normal((S, Tq, Hq, D)).astype(np.float32)
+    k = rng.standard_normal((S, Hkv, L, D)).astype(np.float32)
+    v = rng.standard_normal((S, Hkv, L, D)).astype(np.float32)
+    kw, kd = O.encode_k(k)
+    vp, vd = O.encode_v(v, O.V_Q4_0)
+    causal = O.decode_attention(q, kw, kd, vp, vd, O.V_Q4_0, [L], 0.125, True)
+    for j in range(Tq):
+        n = L - Tq + j + 1
+        one = O.decode_attention(q[:, j:j + 1], kw, kd, vp, vd, O.V_Q4_0, [n], 0.125, False)
+        np.testing.assert_allclose(causal[:, j], one[:, 0], rtol=1e-12, atol=1e-14)
+    perm = rng.permutation(L)
+    flat = O.decode_attention(q, kw, kd, vp, vd, O.V_Q4_0, [L], 0.125, False)
+    flat_p = O.decode_attention(q, kw[:, :, perm], kd[:, :, perm], vp[:, :, perm], vd[:, :, perm],
+                                O.V_Q4_0, [L], 0.125, False)
+    np.testing.assert_allclose(flat, flat_p, rtol=1e-11, atol=1e-14)
+
+
+def test_gqa_groups_are_contiguous():
+    # Hq = 8 over Hkv = 2: heads 0..3 read kv head 0 and 4..7 read kv head 1
+    rng = np.random.default_rng(24)
+    q = rng.standard_normal((1, 1, 8, 32)).astype(np.float32)
+    k = rng.standard_normal((1, 2, 12, 32)).astype(np.float32)
+    v = rng.standard_normal((1, 2, 12, 32)).astype(np.float32)
+    kw, kd = O.encode_k(k)
+    vp, vd = O.encode_v(v, O.V_Q8_0)
+    out = O.decode_attention(q, kw, kd, vp, vd, O.V_Q8_0, [12], 0.3, False)
+    for h in range(8):
+        kvh = h // 4
+        one = O.decode_attention(q[:, :, h:h + 1], kw[:, kvh:kvh + 1], kd[:, kvh:kvh + 1],
+                                 vp[:, kvh:kvh + 1], vd[:, kvh:kvh + 1], O.V_Q8_0, [12], 0.3, False)
+        np.testing.assert_array_equal(out[:, :, h], one[:, :, 0])
+
+
+def test_visible_tokens():
+    assert list(O.visible_tokens(10, 1, True)) == [10]
+    assert list(O.visible_tokens(10, 4, True)) == [7, 8, 9, 10]
+    assert list(O.visible_tokens(10, 4, False)) == [10, 10, 10, 10]
