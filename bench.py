@@ -1,0 +1,189 @@
+"""Decode-attention benchmark on one MI355X.
+
+A step is one pass of the whole hot path on the 128k-context workload
+(1 sequence, 32 query / 8 kv heads, head_dim 128, 131072 tokens, int8 K
+packed 4 per word with fp16 scales, q4_0 V): kv_append_quant writes one new
+token at position 131071, then attn_decode_packed attends over all 131072
+tokens.  Inputs are seeded synthetic data resident in HBM before timing.
+Steps rotate over R cache replicas (default 3, 654 MB) so the 256 MB
+Infinity Cache cannot hold the working set between reuses.
+
+Prints one JSON line: value = algorithmic KV bytes per step / time per step
+(GB/s), with ms and us per step, the roofline of the attention kernel and
+the oracle timed on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(spec, n_tokens: int, append_rows: int) -> dict:
+    """K payload + K scales + V payload + V scales of every attended
+    (token, kv head), plus the packed bytes written by the append."""
+    D = spec.head_dim
+    nb = D // 32
+    kb = D + 2 * nb
+    vb = (D // 2 if spec.v_format == 0 else D) + 2 * nb
+    attn = n_tokens * spec.n_kv_heads * (kb + vb)
+    app = append_rows * spec.n_kv_heads * (kb + vb)
+    return {"attn": attn, "append": app, "step": attn + app, "per_token_head": kb + vb}
+
+
+def cpu_baseline(ci, kv_heads_sample: int) -> dict:
+    """The oracle on the host: the same step (quantize the new token, then
+    attention from the packed cache) for `kv_heads_sample` of the kv heads,
+    scaled to a whole step."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import kvq_oracle as O
+    spec = ci.spec
+    G = spec.n_q_heads // spec.n_kv_heads
+    L = spec.ctx
+    heads = list(range(kv_heads_sample))
+    with threadpool_limits(limits=1):
+        # the packed cache is an input of the step, built outside the timing
+        kw, kd = O.encode_k(ci.k[0][:, heads].transpose(1, 0, 2))
+        vp, vd = O.encode_v(ci.v[0][:, heads].transpose(1, 0, 2), spec.v_format)
+        t0 = time.perf_counter()
+        nk, nkd = O.encode_k(ci.extra["append_k"][0, 0, heads])
+        nv, nvd = O.encode_v(ci.extra["append_v"][0, 0, heads], spec.v_format)
+        kw[:, L - 1], kd[:, L - 1], vp[:, L - 1], vd[:, L - 1] = nk, nkd, nv, nvd
+        q = ci.q[:, :, :kv_heads_sample * G]
+        O.decode_attention(q, kw[None], kd[None], vp[None], vd[None], spec.v_format, ci.seq_len,
+                           spec.sm_scale, False)
+        dt = time.perf_counter() - t0
+    scale = spec.n_kv_heads / kv_heads_sample
+    us = dt * scale * 1e6
+    return {"value": us, "unit": "us/step", "cores": 1, "kind": "oracle",
+            "sample": f"{kv_heads_sample} of {spec.n_kv_heads} kv heads of one step "
+                      f"({dt:.1f} s on the host, numpy float64, BLAS limited to 1 thread), "
+                      f"scaled x{scale:g}"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=3)
+    ap.add_argument("--cpu-sample-heads", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the path is not "
+                                   "sharded across GPUs", "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    import decode_attention_packed_amd as K
+    from decode_attention_packed_amd import workloads as W
+
+    torch.cuda.set_device(0)
+    ci = W.make_inputs("long128k")[0]
+    spec = ci.spec
+    L = spec.ctx
+    print(f"[bench] inputs ready: {spec.name} L={L}", file=sys.stderr, flush=True)
+
+    caches = []
+    for _ in range(args.replicas):
+        c = K.PackedKVCache(spec.n_kv_heads, spec.head_dim, ci.seg_tokens, 1, spec.v_format)
+        kk = torch.from_numpy(ci.k).cuda()
+        vv = torch.from_numpy(ci.v).cuda()
+        K.kv_append_quant(c, kk, vv, torch.zeros(1, dtype=torch.int32, device="cuda"))
+        del kk, vv
+        caches.append(c)
+    torch.cuda.synchronize()
+    q = torch.from_numpy(ci.q).cuda()
+    out = torch.empty_like(q)
+    ak = torch.from_numpy(ci.extra["append_k"]).cuda()
+    av = torch.from_numpy(ci.extra["append_v"]).cuda()
+    pos = torch.tensor([L - 1], dtype=torch.int32, device="cuda")
+    seq_len = torch.tensor([L], dtype=torch.int32, device="cuda")
+    ws_bytes = K.attn_decode_packed_workspace_size(caches[0], 1, 1, spec.n_q_heads, L)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    print(f"[bench] caches built: {args.replicas} x {caches[0].nbytes / 1e6:.1f} MB", file=sys.stderr,
+          flush=True)
+
+    def step(i, ev=None):
+        c = caches[i % len(caches)]
+        K.kv_append_quant(c, ak, av, pos, stream=stream)
+        if ev is not None:
+            ev[0].record(stream)
+        K.attn_decode_packed(c, q, out, seq_len, L, spec.sm_scale, False, ws, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_step = ms_total / args.steps
+
+    # attention call alone, per step, with events on the launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
+
+    nbytes = algorithmic_bytes(spec, L, 1)
+    gbs = nbytes["step"] / (ms_step * 1e-3) / 1e9
+    attn_mean_s = float(attn_ms.mean()) * 1e-3
+    achieved = nbytes["attn"] / attn_mean_s / 1e9
+    result = {
+        "metric": "decode attention µs/step + KV GB/s (% of HBM peak) at 128k ctx, 1 GPU",
+        "value": round(gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8 K x int8 Q dot (int32), q4_0 V, fp32 softmax/accumulate",
+        "data": "synthetic",
+        "config": {"workload": "long128k: 1 seq, 1 query token, 32 q / 8 kv heads, head_dim 128, "
+                               "131072 ctx, K int8+fp16 scale packed 4/u32, V q4_0, 1 append/step",
+                   "replicas": args.replicas, "kv_bytes_per_step": nbytes["step"]},
+        "attn_us": {"mean": round(float(attn_ms.mean()) * 1e3, 2),
+                    "p10": round(float(np.percentile(attn_ms, 10)) * 1e3, 2),
+                    "p50": round(float(np.percentile(attn_ms, 50)) * 1e3, 2),
+                    "p90": round(float(np.percentile(attn_ms, 90)) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+    print(f"[bench] timed: {ms_step * 1e3:.2f} us/step, attention {attn_ms.mean() * 1e3:.2f} us",
+          file=sys.stderr, flush=True)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(ci, args.cpu_sample_heads)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,197 @@
+// C ABI of libkvq: host-side validation, split planning and launches.
+// Every check runs before the first launch, so an error return leaves device
+// memory untouched.  The library keeps no state and never allocates.
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+
+#include "kvq.h"
+#include "kvq_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_cache(const kvq_cache* c) {
+  if (!c) return KVQ_ERR_INVALID;
+  if (c->n_kv_heads < 1 || c->n_segs < 1 || c->reserved != 0) return KVQ_ERR_INVALID;
+  if (c->seg_tokens < KVQ_SEG_ALIGN || c->seg_tokens % KVQ_SEG_ALIGN) return KVQ_ERR_INVALID;
+  if (c->v_format != KVQ_V_Q4_0 && c->v_format != KVQ_V_Q8_0) return KVQ_ERR_INVALID;
+  if (c->head_dim < KVQ_BLOCK || c->head_dim % KVQ_BLOCK) return KVQ_ERR_INVALID;
+  if (c->head_dim != 64 && c->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+  if (!c->k_qs || !c->k_d || !c->v_qs || !c->v_d) return KVQ_ERR_INVALID;
+  if (!aligned16(c->k_qs) || !aligned16(c->k_d) || !aligned16(c->v_qs) || !aligned16(c->v_d))
+    return KVQ_ERR_INVALID;
+  return KVQ_OK;
+}
+
+// Without a segment table, sequence i uses segments i*max_segs .. i*max_segs+max_segs-1.
+int check_segments(const kvq_cache* c, int n_seq, const int32_t* seg_table, int max_segs) {
+  if (max_segs < 1) return KVQ_ERR_INVALID;
+  if (!seg_table && (long long)n_seq * max_segs > c->n_segs) return KVQ_ERR_INVALID;
+  if (seg_table && (reinterpret_cast<uintptr_t>(seg_table) & 3u)) return KVQ_ERR_INVALID;
+  return KVQ_OK;
+}
+
+int check_attn(const kvq_cache* c, const float* q, const float* out, int n_seq, int n_qtok,
+               int n_q_heads, const int32_t* seg_table, int max_segs, const int32_t* seq_len,
+               int max_seq_len) {
+  int st = check_cache(c);
+  if (st) return st;
+  if (!q || !out || !seq_len || !aligned16(q) || !aligned16(out)) return KVQ_ERR_INVALID;
+  if (reinterpret_cast<uintptr_t>(seq_len) & 3u) return KVQ_ERR_INVALID;
+  if (n_seq < 1 || n_qtok < 1 || n_qtok > KVQ_MAX_QTOK || n_q_heads < 1) return KVQ_ERR_INVALID;
+  if (n_q_heads % c->n_kv_heads) return KVQ_ERR_INVALID;
+  if (max_seq_len < n_qtok || (long long)max_seq_len > (long long)max_segs * c->seg_tokens)
+    return KVQ_ERR_INVALID;
+  st = check_segments(c, n_seq, seg_table, max_segs);
+  if (st) return st;
+  return KVQ_OK;
+}
+
+}  // namespace
+
+namespace kvq {
+
+SplitPlan plan_splits(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads, int max_seq_len) {
+  (void)n_qtok;
+  (void)n_q_heads;
+  int chunk = 0;
+  if (const char* env = std::getenv("KVQ_CHUNK_TOKENS")) {
+    chunk = std::atoi(env);
+    if (chunk < KVQ_SEG_ALIGN || chunk % KVQ_SEG_ALIGN) chunk = 0;
+  }
+  if (!chunk) {
+    // Grow the chunk while the grid keeps at least ~8 single-wave groups per CU.
+    const long long target = 2048;
+    chunk = KVQ_SEG_ALIGN;
+    while (chunk < 8192) {
+      const long long next = 2LL * chunk;
+      const long long groups = (long long)n_seq * c.n_kv_heads * ((max_seq_len + next - 1) / next);
+      if (groups < target) break;
+      chunk = (int)next;
+    }
+  }
+  SplitPlan p;
+  p.chunk = chunk;
+  p.n_split = (max_seq_len + chunk - 1) / chunk;
+  return p;
+}
+
+size_t workspace_bytes(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads,
+                       const SplitPlan& plan) {
+  const size_t rows = (size_t)n_seq * n_qtok * n_q_heads;
+  return rows * plan.n_split * (size_t)(c.head_dim + 2) * sizeof(float);
+}
+
+}  // namespace kvq
+
+extern "C" {
+
+int kvq_abi_version(void) { return KVQ_ABI_VERSION; }
+
+const char* kvq_status_string(int status) {
+  switch (status) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_INVALID: return "invalid argument";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_ERR_WORKSPACE: return "workspace too small";
+    case KVQ_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int kvq_cache_bytes(int n_kv_heads, int head_dim, int seg_tokens, int n_segs, int v_format,
+                    size_t out_bytes[4]) {
+  if (!out_bytes || n_kv_heads < 1 || n_segs < 1 || seg_tokens < 1) return KVQ_ERR_INVALID;
+  if (head_dim < KVQ_BLOCK || head_dim % KVQ_BLOCK) return KVQ_ERR_INVALID;
+  if (v_format != KVQ_V_Q4_0 && v_format != KVQ_V_Q8_0) return KVQ_ERR_INVALID;
+  const size_t rows = (size_t)n_segs * n_kv_heads * seg_tokens;
+  const size_t nb = head_dim / KVQ_BLOCK;
+  out_bytes[0] = rows * head_dim;                                   // int8 K codes
+  out_bytes[1] = rows * nb * 2;                                     // fp16 K scales
+  out_bytes[2] = rows * (v_format == KVQ_V_Q4_0 ? head_dim / 2 : head_dim);
+  out_bytes[3] = rows * nb * 2;                                     // fp16 V scales
+  return KVQ_OK;
+}
+
+int kv_append_quant(const kvq_cache* cache, const float* k_new, const float* v_new, int n_seq,
+                    int n_new, const int32_t* seg_table, int max_segs, const int32_t* start_pos,
+                    void* stream) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (!k_new || !v_new || !start_pos || !aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_INVALID;
+  if (reinterpret_cast<uintptr_t>(start_pos) & 3u) return KVQ_ERR_INVALID;
+  if (n_seq < 1 || n_new < 1) return KVQ_ERR_INVALID;
+  if ((long long)n_seq * n_new * cache->n_kv_heads * (cache->head_dim / KVQ_BLOCK) > 0x7fffffffLL)
+    return KVQ_ERR_INVALID;
+  st = check_segments(cache, n_seq, seg_table, max_segs);
+  if (st) return st;
+  const int r = kvq::launch_append(*cache, k_new, v_new, n_seq, n_new, seg_table, max_segs,
+                                   start_pos, static_cast<hipStream_t>(stream));
+  return r ? KVQ_ERR_HIP : KVQ_OK;
+}
+
+int attn_decode_packed_workspace_size(const kvq_cache* cache, int n_seq, int n_qtok, int n_q_heads,
+                                      int max_seq_len, size_t* bytes) {
+  int st = check_cache(cache);
+  if (st) return st;
+  if (!bytes || n_seq < 1 || n_qtok < 1 || n_qtok > KVQ_MAX_QTOK || n_q_heads < 1 ||
+      n_q_heads % cache->n_kv_heads || max_seq_len < n_qtok)
+    return KVQ_ERR_INVALID;
+  const kvq::SplitPlan plan = kvq::plan_splits(*cache, n_seq, n_qtok, n_q_heads, max_seq_len);
+  *bytes = kvq::workspace_bytes(*cache, n_seq, n_qtok, n_q_heads, plan);
+  return KVQ_OK;
+}
+
+int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n_seq, int n_qtok,
+                       int n_q_heads, const int32_t* seg_table, int max_segs,
+                       const int32_t* seq_len, int max_seq_len, float sm_scale, int causal,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_attn(cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
+                      max_seq_len);
+  if (st) return st;
+  if (!std::isfinite(sm_scale)) return KVQ_ERR_INVALID;
+  const int group = n_q_heads / cache->n_kv_heads;
+  if (n_qtok != 1) return KVQ_ERR_UNSUPPORTED;
+  if (!kvq::attn_sq_supported(cache->head_dim, group, cache->v_format)) return KVQ_ERR_UNSUPPORTED;
+  (void)causal;   // one query token at the last position sees every token either way
+  const kvq::SplitPlan plan = kvq::plan_splits(*cache, n_seq, n_qtok, n_q_heads, max_seq_len);
+  const size_t need = kvq::workspace_bytes(*cache, n_seq, n_qtok, n_q_heads, plan);
+  if (workspace_bytes < need || (need && !workspace)) return KVQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KVQ_ERR_INVALID;
+  const int r = kvq::launch_attn_sq(*cache, q, out, n_seq, n_q_heads, seg_table, max_segs, seq_len,
+                                    plan, sm_scale, workspace, static_cast<hipStream_t>(stream));
+  if (r == -2) return KVQ_ERR_UNSUPPORTED;
+  return r ? KVQ_ERR_HIP : KVQ_OK;
+}
+
+int kvq_debug_quant_q(const float* q, int n_rows, int head_dim, int8_t* codes, float* scales,
+                      void* stream) {
+  if (!q || !codes || !scales || !aligned16(q) || !aligned16(codes) || !aligned16(scales))
+    return KVQ_ERR_INVALID;
+  if (n_rows < 1) return KVQ_ERR_INVALID;
+  if (head_dim != 64 && head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+  return kvq::launch_debug_quant_q(q, n_rows, head_dim, codes, scales,
+                                   static_cast<hipStream_t>(stream))
+             ? KVQ_ERR_HIP
+             : KVQ_OK;
+}
+
+int kvq_debug_qk_isum(const kvq_cache* cache, const float* q, int n_seq, int n_qtok, int n_q_heads,
+                      const int32_t* seg_table, int max_segs, const int32_t* seq_len,
+                      int max_seq_len, int32_t* isum, void* stream) {
+  int st = check_attn(cache, q, q, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
+                      max_seq_len);
+  if (st) return st;
+  if (!isum || !aligned16(isum)) return KVQ_ERR_INVALID;
+  return kvq::launch_debug_isum(*cache, q, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
+                                max_seq_len, isum, static_cast<hipStream_t>(stream))
+             ? KVQ_ERR_HIP
+             : KVQ_OK;
+}
+
+}  // extern "C"

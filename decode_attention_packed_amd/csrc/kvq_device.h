@@ -1,0 +1,114 @@
+// Device-side helpers shared by the libkvq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+constexpr int kBlock = 32;   // elements per quantization block along head_dim
+
+// fp32 -> binary16 bits with the hardware conversion (round to nearest even,
+// binary16 subnormals kept).
+__device__ __forceinline__ uint16_t f32_to_half_bits(float x) {
+  _Float16 h = (_Float16)x;
+  return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ float half_bits_to_f32(uint16_t b) {
+  return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Integer code of x for scale d: the fp32 quotient (correctly rounded
+// division), rounded to nearest even, clamped to [lo, hi]; 0 when d == 0.
+__device__ __forceinline__ int quant_code(float x, float d, float lo, float hi) {
+  if (d == 0.0f) return 0;
+  float r = rintf(x / d);
+  return (int)fminf(fmaxf(r, lo), hi);
+}
+
+// Cross-lane moves.  DPP controls (gfx9 encoding): quad_perm [1,0,3,2] = 0xB1
+// (lane ^ 1), quad_perm [2,3,0,1] = 0x4E (lane ^ 2), row_half_mirror = 0x141
+// (lane i <-> 7-i inside each 8), row_ror:8 = 0x128 (lane ^ 8 inside a row).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int mask) {
+  int lane = __lane_id();
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, x)));
+}
+
+// Sum over the PARTS consecutive lanes that share one token (PARTS = 4 or 8);
+// every lane of the group receives the total.
+template <int PARTS>
+__device__ __forceinline__ float sum_parts(float x) {
+  x += dpp_f<0xB1>(x);
+  x += dpp_f<0x4E>(x);
+  if constexpr (PARTS == 8) x += dpp_f<0x141>(x);
+  return x;
+}
+template <int PARTS>
+__device__ __forceinline__ int isum_pair(int x) {
+  static_assert(PARTS >= 2, "");
+  return x + dpp_i<0xB1>(x);
+}
+
+// Reduce over the token slots of a wave (lanes that differ in the bits above
+// log2(PARTS)); every lane receives the result.
+template <int PARTS>
+__device__ __forceinline__ float max_slots(float x) {
+  if constexpr (PARTS == 4) x = fmaxf(x, dpp_f<0x128 - 4>(x));   // row_ror:4 -> lane ^ 4 after quad max
+  x = fmaxf(x, dpp_f<0x128>(x));
+  x = fmaxf(x, shfl_xor_f(x, 16));
+  x = fmaxf(x, shfl_xor_f(x, 32));
+  return x;
+}
+template <int PARTS>
+__device__ __forceinline__ float sum_slots(float x) {
+  if constexpr (PARTS == 4) x += dpp_f<0x128 - 4>(x);
+  x += dpp_f<0x128>(x);
+  x += shfl_xor_f(x, 16);
+  x += shfl_xor_f(x, 32);
+  return x;
+}
+
+// Quantize `n` (a multiple of 64) consecutive fp32 values of Q with one wave:
+// per 32-block a = max|x|, d = a / 127 kept in fp32, codes as quant_code.
+// Codes go to `codes` (n bytes) and scales to `scales` (n / 32 floats); both
+// may be LDS or global.  Lanes 0..31 and 32..63 each cover one block per step.
+__device__ __forceinline__ void quantize_q_wave(const float* src, int n, int8_t* codes,
+                                                float* scales) {
+  const int lane = __lane_id();
+  for (int e0 = 0; e0 < n; e0 += 64) {
+    const float x = src[e0 + lane];
+    float a = fabsf(x);
+    a = fmaxf(a, shfl_xor_f(a, 1));
+    a = fmaxf(a, shfl_xor_f(a, 2));
+    a = fmaxf(a, shfl_xor_f(a, 4));
+    a = fmaxf(a, shfl_xor_f(a, 8));
+    a = fmaxf(a, shfl_xor_f(a, 16));
+    const float d = a / 127.0f;
+    codes[e0 + lane] = (int8_t)quant_code(x, d, -127.0f, 127.0f);
+    if ((lane & 31) == 0) scales[(e0 + lane) / kBlock] = d;
+  }
+}
+
+__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int acc) {
+  return __builtin_amdgcn_sdot4((int)a, (int)b, acc, false);
+}
+
+// Segment lookup for token t of sequence `seq`.
+__device__ __forceinline__ int segment_of(const int32_t* seg_table, int seq, int max_segs,
+                                          int segj) {
+  return seg_table ? seg_table[seq * max_segs + segj] : seq * max_segs + segj;
+}
+
+}  // namespace kvq

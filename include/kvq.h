@@ -1,0 +1,165 @@
+/*
+ * kvq.h - C ABI of libkvq: decode attention over a packed, quantized KV cache
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation comes from "Flash Attention for llama.cpp on RDNA3 ...
+ * Part 1" (page 1): K is stored as an 8-bit payload packed four values to a
+ * 32-bit word plus an fp16 scale, re-packed as tokens arrive, and QK^T runs as
+ * packed int8 dot products; V is kept as q4_0 or q8_0 blocks (body text and
+ * the two KLD tables).  The 47% K saving in that page's title fixes the block
+ * at 32 elements with one fp16 scale.  Append-only segments follow "BitLLM"
+ * (page 3), section "how it differs"; nibble placement follows its section
+ * "how to use" (two aligned 4-bit values per byte).
+ *
+ * Conventions for every entry point:
+ *  - Return KVQ_OK (0) or a negative kvq_status.  All arguments are checked on
+ *    the host before anything is launched, so an error return has no side
+ *    effects on device memory.
+ *  - Pointers named "device" point to GPU memory owned by the caller; the
+ *    library never allocates, frees, synchronizes, prints or keeps state.
+ *    Device pointers must be 16-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously on it; device faults surface at the caller's next sync.
+ *  - Contents of device index arrays (segment tables, lengths, positions) are
+ *    preconditions and are not checked.  Inputs must be finite.
+ *  - Calls are reentrant; concurrent calls that write the same cache rows or
+ *    the same workspace race.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+#define KVQ_BLOCK 32            /* elements per quantization block along head_dim */
+#define KVQ_SEG_ALIGN 64        /* seg_tokens must be a positive multiple of this */
+#define KVQ_MAX_QTOK 16         /* largest query-token count per sequence (verify) */
+
+enum kvq_status {
+  KVQ_OK = 0,
+  KVQ_ERR_INVALID = -1,      /* bad pointer, alignment, shape or value */
+  KVQ_ERR_UNSUPPORTED = -2,  /* valid but not built: head_dim, group size, format */
+  KVQ_ERR_WORKSPACE = -3,    /* workspace missing or smaller than required */
+  KVQ_ERR_HIP = -4           /* the HIP runtime reported a launch error */
+};
+
+enum kvq_v_format {
+  KVQ_V_Q4_0 = 0,  /* 32-block: fp16 d, 16 bytes; value = d * (nibble - 8) */
+  KVQ_V_Q8_0 = 1   /* 32-block: fp16 d, 32 int8 codes; value = d * code */
+};
+
+/*
+ * A packed KV cache.  All four planes are device memory owned by the caller,
+ * laid out [n_segs][n_kv_heads][seg_tokens][...] with one token row per line:
+ *   k_qs  uint32 [..][head_dim/4]   int8 K codes, byte k of word w = element 4w+k
+ *   k_d   uint16 [..][head_dim/32]  fp16 bit patterns, one per 32-block
+ *   v_qs  uint8  [..][head_dim/2]   (q4_0) byte j of a block = element j | element j+16 << 4
+ *         uint8  [..][head_dim]     (q8_0) int8 codes
+ *   v_d   uint16 [..][head_dim/32]  fp16 bit patterns
+ * Token t of sequence i lives in segment seg_table[i*max_segs + t/seg_tokens]
+ * (or segment i*max_segs + t/seg_tokens when no table is given), at row
+ * t % seg_tokens.  A contiguous cache is one segment per sequence.
+ * K codes: a = max|x|, d = fp16(a/127), c = clamp(rne(x/d), -127, 127).
+ * q4_0:    m = first element of largest |x|, d = fp16(m/-8),
+ *          n = clamp(rne(x/d) + 8, 0, 15).   q8_0 is the K rule.
+ */
+typedef struct kvq_cache {
+  int32_t n_kv_heads;   /* >= 1 */
+  int32_t head_dim;     /* 64 or 128 */
+  int32_t seg_tokens;   /* tokens per segment, multiple of KVQ_SEG_ALIGN */
+  int32_t n_segs;       /* segments in each plane */
+  int32_t v_format;     /* enum kvq_v_format */
+  int32_t reserved;     /* must be 0 */
+  uint32_t* k_qs;       /* device */
+  uint16_t* k_d;        /* device */
+  uint8_t* v_qs;        /* device */
+  uint16_t* v_d;        /* device */
+} kvq_cache;
+
+/* ABI version of the loaded library (KVQ_ABI_VERSION). */
+int kvq_abi_version(void);
+
+/* Static text for a status code; never NULL. */
+const char* kvq_status_string(int status);
+
+/*
+ * Bytes of each plane (k_qs, k_d, v_qs, v_d) for a cache of the given shape,
+ * written to out_bytes[0..3] (host array).  Host only.  Per token and kv head
+ * K takes head_dim + 2*head_dim/32 bytes, i.e. 34 bytes per 32 elements, which
+ * is the 47% saving over fp16 K given in page 1's title (1 - 34/64).
+ */
+int kvq_cache_bytes(int n_kv_heads, int head_dim, int seg_tokens, int n_segs,
+                    int v_format, size_t out_bytes[4]);
+
+/*
+ * kv_append_quant: quantize and pack new K/V rows into the cache (page 1:
+ * the K payload is re-packed as it is written; V is written as q4_0/q8_0).
+ *   k_new, v_new  device float [n_seq][n_new][n_kv_heads][head_dim]
+ *   start_pos     device int32 [n_seq]; row j of sequence i goes to token
+ *                 start_pos[i] + j, which must be < max_segs*seg_tokens and
+ *                 must map to a segment < n_segs
+ *   seg_table     device int32 [n_seq][max_segs] or NULL (see kvq_cache)
+ * Output bits are a pure function of the inputs (bit-exact, deterministic).
+ * Rows of different calls or sequences must not target the same token.
+ */
+int kv_append_quant(const kvq_cache* cache, const float* k_new, const float* v_new,
+                    int n_seq, int n_new, const int32_t* seg_table, int max_segs,
+                    const int32_t* start_pos, void* stream);
+
+/*
+ * Workspace bytes attn_decode_packed needs for this shape (host only).  The
+ * workspace holds per-split softmax partials; it is caller-owned device
+ * memory, not read before written, and may be reused between calls on one
+ * stream.
+ */
+int attn_decode_packed_workspace_size(const kvq_cache* cache, int n_seq, int n_qtok,
+                                      int n_q_heads, int max_seq_len, size_t* bytes);
+
+/*
+ * attn_decode_packed: one decode step of attention over the packed cache.
+ *   q        device float [n_seq][n_qtok][n_q_heads][head_dim]
+ *   out      device float [n_seq][n_qtok][n_q_heads][head_dim]
+ *   seq_len  device int32 [n_seq], each in [max(1, n_qtok), max_seq_len]
+ *   max_seq_len  host bound on seq_len (sizes the split grid)
+ *   sm_scale softmax scale (1/sqrt(head_dim) in the usual model)
+ *   causal   if nonzero, query j sits at position seq_len - n_qtok + j and
+ *            sees tokens up to and including that position; otherwise every
+ *            query sees all seq_len tokens
+ * Query head h reads kv head h / (n_q_heads / n_kv_heads).  Q is quantized to
+ * int8 per 32-block with an fp32 scale (a = max|q|, d = a/127, codes as for K),
+ * QK^T is summed in int32 per block and rescaled in fp32, softmax runs per
+ * context split with an online maximum, V is dequantized inside the
+ * weighted sum, and a second pass merges the splits.  n_qtok is 1..16.
+ */
+int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n_seq,
+                       int n_qtok, int n_q_heads, const int32_t* seg_table, int max_segs,
+                       const int32_t* seq_len, int max_seq_len, float sm_scale, int causal,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Test hooks: expose the integer stages of the hot path so they can be
+ * compared bit for bit with a reference.
+ * kvq_debug_quant_q: Q quantization exactly as the attention kernels do it.
+ *   q       device float [n_rows][head_dim]
+ *   codes   device int8  [n_rows][head_dim]
+ *   scales  device float [n_rows][head_dim/32]
+ * kvq_debug_qk_isum: per-block int32 sums of Q codes times K codes.
+ *   isum    device int32 [n_seq][n_qtok][n_q_heads][max_seq_len][head_dim/32];
+ *           entries for tokens >= seq_len[i] are left untouched.
+ */
+int kvq_debug_quant_q(const float* q, int n_rows, int head_dim, int8_t* codes, float* scales,
+                      void* stream);
+int kvq_debug_qk_isum(const kvq_cache* cache, const float* q, int n_seq, int n_qtok,
+                      int n_q_heads, const int32_t* seg_table, int max_segs,
+                      const int32_t* seq_len, int max_seq_len, int32_t* isum, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

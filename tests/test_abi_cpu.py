@@ -1,0 +1,113 @@
+"""Host-side checks of the C ABI: the library loads, exports every function
+include/kvq.h declares, sizes caches by the closed form, and rejects bad
+arguments before touching the GPU (none of these calls reaches HIP)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import decode_attention_packed_amd as K
+from decode_attention_packed_amd._lib import KvqCacheStruct
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert "attn_decode_packed" in names and "kv_append_quant" in names
+    L = K.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(K.EXPORTS) == names
+
+
+def test_abi_version_and_status_strings():
+    assert K.kvq_abi_version() == 1
+    assert K.status_string(0) == "ok"
+    assert K.status_string(K.KVQ_ERR_WORKSPACE) == "workspace too small"
+    assert K.status_string(12345) == "unknown status"
+
+
+def test_cache_bytes_closed_form():
+    kq, kd, vq, vd = K.kvq_cache_bytes(8, 128, 131072, 1, K.KVQ_V_Q4_0)
+    rows = 8 * 131072
+    assert (kq, kd, vq, vd) == (rows * 128, rows * 8, rows * 64, rows * 8)
+    # K bytes per element: 34 per 32 -> 1 - 34/64 = 46.875% below fp16 (the 47% of page 1)
+    assert 1 - (kq + kd) / (rows * 128 * 2) == 1 - 34 / 64
+    kq, kd, vq, vd = K.kvq_cache_bytes(32, 64, 4096, 35, K.KVQ_V_Q8_0)
+    assert vq == 35 * 32 * 4096 * 64 and vd == kd
+    with pytest.raises(K.KvqError):
+        K.kvq_cache_bytes(8, 100, 64, 1, 0)
+    with pytest.raises(K.KvqError):
+        K.kvq_cache_bytes(8, 128, 64, 1, 7)
+
+
+def _fake_cache(**kw):
+    args = dict(n_kv_heads=8, head_dim=128, seg_tokens=1024, n_segs=1, v_format=0, reserved=0,
+                k_qs=0x1000, k_d=0x2000, v_qs=0x3000, v_d=0x4000)
+    args.update(kw)
+    return KvqCacheStruct(**args)
+
+
+def _attn(c, q=0x5000, out=0x6000, n_seq=1, n_qtok=1, hq=32, table=None, max_segs=1,
+          seq_len=0x7000, max_len=1024, scale=0.1, ws=0x8000, ws_bytes=1 << 30):
+    L = K.lib()
+    return L.attn_decode_packed(ctypes.byref(c), q, out, n_seq, n_qtok, hq, table, max_segs, seq_len,
+                                max_len, scale, 0, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=96), K.KVQ_ERR_UNSUPPORTED),
+    (dict(head_dim=100), K.KVQ_ERR_INVALID),
+    (dict(seg_tokens=100), K.KVQ_ERR_INVALID),
+    (dict(v_format=3), K.KVQ_ERR_INVALID),
+    (dict(reserved=1), K.KVQ_ERR_INVALID),
+    (dict(k_qs=0x1004), K.KVQ_ERR_INVALID),
+    (dict(v_d=None), K.KVQ_ERR_INVALID),
+    (dict(n_kv_heads=0), K.KVQ_ERR_INVALID),
+])
+def test_bad_cache_rejected(kw, status):
+    assert _attn(_fake_cache(**kw)) == status
+
+
+def test_bad_attention_args_rejected():
+    c = _fake_cache()
+    assert _attn(c, hq=12) == K.KVQ_ERR_INVALID              # not a multiple of n_kv_heads
+    assert _attn(c, hq=8 * 3) == K.KVQ_ERR_UNSUPPORTED       # group of 3 not built
+    assert _attn(c, n_qtok=17) == K.KVQ_ERR_INVALID
+    assert _attn(c, max_len=2048) == K.KVQ_ERR_INVALID       # beyond max_segs * seg_tokens
+    assert _attn(c, n_seq=2) == K.KVQ_ERR_INVALID            # no table and too few segments
+    assert _attn(c, q=0x5008) == K.KVQ_ERR_INVALID           # misaligned
+    assert _attn(c, seq_len=None) == K.KVQ_ERR_INVALID
+    assert _attn(c, scale=float("nan")) == K.KVQ_ERR_INVALID
+    assert _attn(c, ws_bytes=16) == K.KVQ_ERR_WORKSPACE
+    assert _attn(c, ws=None) == K.KVQ_ERR_WORKSPACE
+
+
+def test_workspace_size_is_host_only():
+    c = _fake_cache(seg_tokens=131072)
+    out = ctypes.c_size_t(0)
+    assert K.lib().attn_decode_packed_workspace_size(ctypes.byref(c), 1, 1, 32, 131072,
+                                                      ctypes.byref(out)) == 0
+    assert out.value > 0 and out.value % 4 == 0
+    assert K.lib().attn_decode_packed_workspace_size(ctypes.byref(c), 1, 1, 30, 131072,
+                                                      ctypes.byref(out)) == K.KVQ_ERR_INVALID
+
+
+def test_bad_append_args_rejected():
+    c = _fake_cache()
+    L = K.lib()
+    f = L.kv_append_quant
+    assert f(ctypes.byref(c), None, 0x2000, 1, 1, None, 1, 0x3000, None) == K.KVQ_ERR_INVALID
+    assert f(ctypes.byref(c), 0x1000, 0x2000, 0, 1, None, 1, 0x3000, None) == K.KVQ_ERR_INVALID
+    assert f(ctypes.byref(c), 0x1000, 0x2000, 2, 1, None, 1, 0x3000, None) == K.KVQ_ERR_INVALID
+    assert f(ctypes.byref(c), 0x1000, 0x2000, 1, 1, None, 1, 0x3002, None) == K.KVQ_ERR_INVALID
+    assert f(ctypes.byref(_fake_cache(head_dim=256)), 0x1000, 0x2000, 1, 1, None, 1, 0x3000,
+             None) == K.KVQ_ERR_UNSUPPORTED

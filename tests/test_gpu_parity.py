@@ -1,0 +1,219 @@
+"""GPU parity: the HIP path (through the C ABI) against the oracle.
+
+Quantize/pack output, Q codes and per-block integer sums are compared bit
+for bit; attention outputs must be within max |err| 2e-3 and relative L2
+1e-3 of the oracle on the same seeded inputs."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import decode_attention_packed_amd as K  # noqa: E402
+from decode_attention_packed_amd import workloads as W  # noqa: E402
+from oracle import kvq_oracle as O  # noqa: E402
+from tests import gpu_helpers as H  # noqa: E402
+
+
+def _say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# append: bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "gqa8k", "ragged"])
+def test_append_bitexact_full(name):
+    for ci in W.make_inputs(name):
+        _say(f"append {ci.spec.name}")
+        cache, table, max_segs = H.build_cache(ci)
+        torch.cuda.synchronize()
+        for i in range(ci.spec.n_seq):
+            toks = np.arange(int(ci.seq_len[i]))
+            got = H.gpu_rows(cache, ci, i, toks)
+            want = H.oracle_rows(ci, i, toks)
+            for g, w, nm in zip(got, want, ("k_qs", "k_d", "v_qs", "v_d")):
+                assert g.shape == w.shape, nm
+                assert np.array_equal(g, w), (ci.spec.name, i, nm, int((g != w).sum()))
+
+
+def test_append_token_by_token_equals_bulk():
+    ci = W.make_inputs("tiny", ctx=200)[0]
+    bulk, _, _ = H.build_cache(ci)
+    spec = ci.spec
+    step = K.PackedKVCache(spec.n_kv_heads, spec.head_dim, bulk.seg_tokens, 1, spec.v_format)
+    for t in range(200):
+        kk = H.dev(ci.k[:, t:t + 1])
+        vv = H.dev(ci.v[:, t:t + 1])
+        K.kv_append_quant(step, kk, vv, torch.tensor([t], dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    for a, b in ((bulk.k_qs, step.k_qs), (bulk.k_d, step.k_d), (bulk.v_qs, step.v_qs), (bulk.v_d, step.v_d)):
+        assert torch.equal(a[:, :, :200], b[:, :, :200])
+
+
+def test_append_edge_blocks_bitexact():
+    # zero blocks, exact ties, tiny values, large values, sign mixtures
+    rng = np.random.default_rng(7)
+    D, Hkv, n = 128, 2, 64
+    k = rng.standard_normal((1, n, Hkv, D)).astype(np.float32)
+    k[0, 0] = 0.0
+    k[0, 1, :, :32] = np.float32(-0.0)
+    k[0, 2] = (np.arange(D) % 32 - 15.5).astype(np.float32)      # ties at d = 1/8 steps
+    k[0, 3] *= np.float32(1e-6)
+    k[0, 4] *= np.float32(3e3)
+    k[0, 5, :, 0] = 127.0
+    k[0, 5, :, 1:32] = np.arange(31, dtype=np.float32) + 0.5
+    for fmt in (O.V_Q4_0, O.V_Q8_0):
+        cache = K.PackedKVCache(Hkv, D, 64, 1, fmt)
+        K.kv_append_quant(cache, H.dev(k), H.dev(k), torch.zeros(1, dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        kq = cache.k_qs[0].cpu().numpy().view(np.uint32)
+        kd = cache.k_d[0].cpu().numpy().view(np.uint16)
+        vq = cache.v_qs[0].cpu().numpy()
+        vd = cache.v_d[0].cpu().numpy().view(np.uint16)
+        kw, kdd = O.encode_k(k[0].transpose(1, 0, 2))
+        vp, vdd = O.encode_v(k[0].transpose(1, 0, 2), fmt)
+        assert np.array_equal(kq, kw) and np.array_equal(kd, kdd)
+        assert np.array_equal(vq, vp) and np.array_equal(vd, vdd)
+
+
+def test_append_full_size_sampled_rows():
+    # long-context cache at full size: bulk append, then check 4096 sampled rows
+    ci = W.make_inputs("long128k")[0]
+    _say("append long128k full size")
+    cache, _, _ = H.build_cache(ci)
+    torch.cuda.synchronize()
+    toks = np.sort(np.random.default_rng(0).choice(ci.spec.ctx, 4096, replace=False))
+    toks[-1] = ci.spec.ctx - 1
+    got = H.gpu_rows(cache, ci, 0, toks)
+    want = H.oracle_rows(ci, 0, toks)
+    for g, w in zip(got, want):
+        assert np.array_equal(g, w)
+
+
+# ---------------------------------------------------------------------------
+# Q quantization and per-block integer sums: bit-exact
+# ---------------------------------------------------------------------------
+
+def test_quant_q_bitexact():
+    rng = np.random.default_rng(8)
+    for D in (64, 128):
+        q = rng.standard_normal((300, D)).astype(np.float32)
+        q[0] = 0
+        q[1] *= np.float32(1e-5)
+        q[2] = (np.arange(D) % 32 - 15.5).astype(np.float32)
+        q[3, :32] = 127.0 * (np.arange(32) % 2 * 2 - 1)
+        q[4] *= np.float32(5e3)
+        codes = torch.empty((300, D), dtype=torch.int8, device="cuda")
+        scales = torch.empty((300, D // 32), dtype=torch.float32, device="cuda")
+        K.kvq_debug_quant_q(H.dev(q), codes, scales)
+        torch.cuda.synchronize()
+        wc, wd = O.quantize_q(q)
+        assert np.array_equal(codes.cpu().numpy(), wc)
+        assert np.array_equal(scales.cpu().numpy().view(np.uint32), wd.view(np.uint32))
+
+
+@pytest.mark.parametrize("name", ["tiny", "gqa8k", "ragged"])
+def test_qk_isum_bitexact(name):
+    ci = W.make_inputs(name, ctx=None if name != "ragged" else 3000)[0]
+    cache, table, max_segs = H.build_cache(ci)
+    spec = ci.spec
+    mx = int(ci.seq_len.max())
+    isum = torch.zeros((spec.n_seq, spec.n_qtok, spec.n_q_heads, mx, spec.head_dim // 32),
+                       dtype=torch.int32, device="cuda")
+    if table is None:
+        table = torch.arange(spec.n_seq, dtype=torch.int32, device="cuda")[:, None]
+    K.kvq_debug_qk_isum(cache, H.dev(ci.q), H.dev(ci.seq_len), mx, isum, seg_table=table)
+    torch.cuda.synchronize()
+    got = isum.cpu().numpy()
+    qc, _ = O.quantize_q(ci.q)
+    G = spec.n_q_heads // spec.n_kv_heads
+    for i in range(spec.n_seq):
+        L = int(ci.seq_len[i])
+        kc, _ = O.quantize_k(H.seq_rows(ci, i, "k"))          # [L][Hkv][D]
+        for h in range(spec.n_q_heads):
+            want = O.block_isum(qc[i, 0, h][None, :], kc[:, h // G])   # [L][B]
+            assert np.array_equal(got[i, 0, h, :L], want), (name, i, h)
+
+
+# ---------------------------------------------------------------------------
+# attention parity
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["tiny", "gqa8k", "ragged"])
+def test_attention_parity(name):
+    for ci in W.make_inputs(name):
+        _say(f"attention {ci.spec.name}")
+        cache, table, max_segs = H.build_cache(ci)
+        got = H.run_attention(cache, ci, table, max_segs)
+        ref = H.oracle_attention(ci)
+        H.assert_close(got, ref, ci.spec.name)
+
+
+def test_attention_parity_long128k_step():
+    """The long-context step at full size: append one token at the last
+    position, then attend over all 131072 tokens; the oracle checks the
+    query heads of kv heads 0 and 5 (one head computed one by one is the
+    same computation for every head)."""
+    ci = W.make_inputs("long128k")[0]
+    _say("attention long128k full size")
+    cache, table, max_segs = H.build_cache(ci)
+    L = ci.spec.ctx
+    ak, av = ci.extra["append_k"], ci.extra["append_v"]
+    K.kv_append_quant(cache, H.dev(ak), H.dev(av), torch.tensor([L - 1], dtype=torch.int32, device="cuda"))
+    got = H.run_attention(cache, ci, table, max_segs)
+    ci.k = ci.k.copy()
+    ci.v = ci.v.copy()
+    ci.k[:, L - 1] = ak[:, 0]
+    ci.v[:, L - 1] = av[:, 0]
+    ref = H.oracle_attention(ci, q_heads=list(range(0, 4)) + list(range(20, 24)))
+    H.assert_close(got, ref, "long128k")
+
+
+@pytest.mark.parametrize("D,G,fmt,L", [(128, 1, 0, 1), (128, 2, 1, 63), (128, 8, 0, 777),
+                                       (64, 1, 1, 4097), (64, 4, 0, 130), (128, 4, 1, 2049),
+                                       (64, 8, 1, 65), (128, 4, 0, 3)])
+def test_attention_shapes_and_ragged_tails(D, G, fmt, L):
+    rng = np.random.default_rng(D * 1000 + G * 10 + fmt + L)
+    Hkv = 2
+    spec = W.CacheSpec("edge", 1, 1, G * Hkv, Hkv, D, L, fmt)
+    cap = -(-L // 64) * 64 + 64
+    ci = W.CacheInputs(spec, rng.standard_normal((1, 1, G * Hkv, D)).astype(np.float32),
+                       (rng.standard_normal((1, L, Hkv, D)) * 2).astype(np.float32),
+                       rng.standard_normal((1, L, Hkv, D)).astype(np.float32),
+                       np.array([L], np.int32), None, 1, cap)
+    cache, table, max_segs = H.build_cache(ci)
+    got = H.run_attention(cache, ci, table, max_segs)
+    H.assert_close(got, H.oracle_attention(ci), f"D{D} G{G} f{fmt} L{L}")
+
+
+def test_attention_deterministic():
+    ci = W.make_inputs("gqa8k")[0]
+    cache, table, max_segs = H.build_cache(ci)
+    a = H.run_attention(cache, ci, table, max_segs)
+    b = H.run_attention(cache, ci, table, max_segs)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_attention_errors_leave_output_untouched():
+    ci = W.make_inputs("tiny", ctx=128)[0]
+    cache, table, max_segs = H.build_cache(ci)
+    q = H.dev(ci.q)
+    out = torch.full_like(q, 7.0)
+    sl = H.dev(ci.seq_len)
+    need = K.attn_decode_packed_workspace_size(cache, 1, 1, 4, 128)
+    small = torch.empty(max(need - 16, 16), dtype=torch.uint8, device="cuda")
+    with pytest.raises(K.KvqError) as e:
+        K.attn_decode_packed(cache, q, out, sl, 128, 0.1, False, small)
+    assert e.value.status == K.KVQ_ERR_WORKSPACE
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    with pytest.raises(K.KvqError) as e:
+        K.attn_decode_packed(cache, q, out, sl, 100000, 0.1, False, ws)
+    assert e.value.status == K.KVQ_ERR_INVALID
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
