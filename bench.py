@@ -112,7 +112,7 @@ def main() -> int:
     pos = torch.tensor([L - 1], dtype=torch.int32, device="cuda")
     seq_len = torch.tensor([L], dtype=torch.int32, device="cuda")
     ws_bytes = K.attn_decode_packed_workspace_size(caches[0], 1, 1, spec.n_q_heads, L)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")   # counters start at zero
     stream = torch.cuda.current_stream()
     print(f"[bench] caches built: {args.replicas} x {caches[0].nbytes / 1e6:.1f} MB", file=sys.stderr,
           flush=True)

@@ -59,32 +59,44 @@ namespace kvq {
 SplitPlan plan_splits(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads, int max_seq_len) {
   (void)n_qtok;
   (void)n_q_heads;
+  auto splits = [&](long long chunk) { return (max_seq_len + chunk - 1) / chunk; };
   int chunk = 0;
   if (const char* env = std::getenv("KVQ_CHUNK_TOKENS")) {
     chunk = std::atoi(env);
-    if (chunk < KVQ_SEG_ALIGN || chunk % KVQ_SEG_ALIGN) chunk = 0;
+    if (chunk < kChunkAlign || chunk % kChunkAlign) chunk = 0;
   }
   if (!chunk) {
-    // Grow the chunk while the grid keeps at least ~8 single-wave groups per CU.
-    const long long target = 2048;
-    chunk = KVQ_SEG_ALIGN;
-    while (chunk < 8192) {
+    // Grow the chunk while at least ~2 work-groups per CU remain and the
+    // longest sequence still spreads over 8 or more of them.
+    const long long target_groups = 512;
+    chunk = kChunkAlign;
+    while (chunk < (1 << 20)) {
       const long long next = 2LL * chunk;
-      const long long groups = (long long)n_seq * c.n_kv_heads * ((max_seq_len + next - 1) / next);
-      if (groups < target) break;
+      const long long groups = (long long)n_seq * c.n_kv_heads * splits(next);
+      if (groups < target_groups || splits(next) < 8) break;
       chunk = (int)next;
     }
   }
+  // the split merge stages at most kMaxSplits partials per (sequence, kv head)
+  while (splits(chunk) > kMaxSplits) chunk *= 2;
   SplitPlan p;
   p.chunk = chunk;
-  p.n_split = (max_seq_len + chunk - 1) / chunk;
+  p.n_split = (int)splits(chunk);
   return p;
 }
 
-size_t workspace_bytes(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads,
-                       const SplitPlan& plan) {
-  const size_t rows = (size_t)n_seq * n_qtok * n_q_heads;
-  return rows * plan.n_split * (size_t)(c.head_dim + 2) * sizeof(float);
+static size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WorkspaceLayout workspace_layout(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads,
+                                 const SplitPlan& plan) {
+  const size_t rows = (size_t)n_qtok * (n_q_heads / c.n_kv_heads);
+  const size_t groups = (size_t)n_seq * c.n_kv_heads;
+  WorkspaceLayout w;
+  w.counters = 0;
+  w.part_o = round256(groups * sizeof(unsigned));
+  w.part_ml = w.part_o + round256(groups * plan.n_split * rows * c.head_dim * sizeof(float));
+  w.total = w.part_ml + round256(groups * plan.n_split * rows * 2 * sizeof(float));
+  return w;
 }
 
 }  // namespace kvq
@@ -126,7 +138,7 @@ int kv_append_quant(const kvq_cache* cache, const float* k_new, const float* v_n
   if (!k_new || !v_new || !start_pos || !aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_INVALID;
   if (reinterpret_cast<uintptr_t>(start_pos) & 3u) return KVQ_ERR_INVALID;
   if (n_seq < 1 || n_new < 1) return KVQ_ERR_INVALID;
-  if ((long long)n_seq * n_new * cache->n_kv_heads * (cache->head_dim / KVQ_BLOCK) > 0x7fffffffLL)
+  if ((long long)n_seq * n_new * cache->n_kv_heads * cache->head_dim > 0x7fffff00LL)
     return KVQ_ERR_INVALID;
   st = check_segments(cache, n_seq, seg_table, max_segs);
   if (st) return st;
@@ -142,8 +154,9 @@ int attn_decode_packed_workspace_size(const kvq_cache* cache, int n_seq, int n_q
   if (!bytes || n_seq < 1 || n_qtok < 1 || n_qtok > KVQ_MAX_QTOK || n_q_heads < 1 ||
       n_q_heads % cache->n_kv_heads || max_seq_len < n_qtok)
     return KVQ_ERR_INVALID;
+  if (n_qtok * (n_q_heads / cache->n_kv_heads) > KVQ_MAX_QTOK) return KVQ_ERR_UNSUPPORTED;
   const kvq::SplitPlan plan = kvq::plan_splits(*cache, n_seq, n_qtok, n_q_heads, max_seq_len);
-  *bytes = kvq::workspace_bytes(*cache, n_seq, n_qtok, n_q_heads, plan);
+  *bytes = kvq::workspace_layout(*cache, n_seq, n_qtok, n_q_heads, plan).total;
   return KVQ_OK;
 }
 
@@ -156,16 +169,15 @@ int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n
   if (st) return st;
   if (!std::isfinite(sm_scale)) return KVQ_ERR_INVALID;
   const int group = n_q_heads / cache->n_kv_heads;
-  if (n_qtok != 1) return KVQ_ERR_UNSUPPORTED;
-  if (!kvq::attn_sq_supported(cache->head_dim, group, cache->v_format)) return KVQ_ERR_UNSUPPORTED;
-  (void)causal;   // one query token at the last position sees every token either way
+  if (n_qtok * group > KVQ_MAX_QTOK) return KVQ_ERR_UNSUPPORTED;
+  if (!kvq::attn_supported(cache->head_dim, cache->v_format)) return KVQ_ERR_UNSUPPORTED;
   const kvq::SplitPlan plan = kvq::plan_splits(*cache, n_seq, n_qtok, n_q_heads, max_seq_len);
-  const size_t need = kvq::workspace_bytes(*cache, n_seq, n_qtok, n_q_heads, plan);
-  if (workspace_bytes < need || (need && !workspace)) return KVQ_ERR_WORKSPACE;
+  const size_t need = kvq::workspace_layout(*cache, n_seq, n_qtok, n_q_heads, plan).total;
+  if (workspace_bytes < need || !workspace) return KVQ_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KVQ_ERR_INVALID;
-  const int r = kvq::launch_attn_sq(*cache, q, out, n_seq, n_q_heads, seg_table, max_segs, seq_len,
-                                    plan, sm_scale, workspace, static_cast<hipStream_t>(stream));
-  if (r == -2) return KVQ_ERR_UNSUPPORTED;
+  const int r = kvq::launch_attn(*cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs,
+                                 seq_len, plan, sm_scale, causal ? 1 : 0, workspace,
+                                 static_cast<hipStream_t>(stream));
   return r ? KVQ_ERR_HIP : KVQ_OK;
 }
 
@@ -188,6 +200,7 @@ int kvq_debug_qk_isum(const kvq_cache* cache, const float* q, int n_seq, int n_q
                       max_seq_len);
   if (st) return st;
   if (!isum || !aligned16(isum)) return KVQ_ERR_INVALID;
+  if (n_qtok * (n_q_heads / cache->n_kv_heads) > KVQ_MAX_QTOK) return KVQ_ERR_UNSUPPORTED;
   return kvq::launch_debug_isum(*cache, q, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
                                 max_seq_len, isum, static_cast<hipStream_t>(stream))
              ? KVQ_ERR_HIP

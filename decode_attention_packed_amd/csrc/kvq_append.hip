@@ -3,8 +3,14 @@
 // Page 1 ("Flash Attention for llama.cpp on RDNA3 ... Part 1", summary and
 // first body paragraph): each new K row is re-packed on the fly to int8
 // codes, four per 32-bit word, with an fp16 scale per 32-block; V is written
-// as q4_0 or q8_0 blocks.  One thread owns one 32-block of one row and
-// writes K (8 words + scale) and V (16 or 32 bytes + scale) for it.
+// as q4_0 or q8_0 blocks.  32 lanes own one 32-block of one row, one element
+// per lane; block maxima come from cross-lane reductions.
+//
+// K rows are stored token-major.  V payload and V scales are stored
+// token-interleaved in tiles of 32 tokens ("BitLLM" page 3, section on what
+// differs: the layout follows the reduction axis, T for S.V): inside a tile,
+// byte k of the per-token row of token t sits at k * 32 + t, and scale b of
+// token t at b * 32 + t.
 
 #include "kvq_device.h"
 #include "kvq_launch.h"
@@ -14,13 +20,13 @@ namespace kvq {
 struct AppendParams {
   const float* k_new;
   const float* v_new;
-  uint32_t* k_qs;
+  uint8_t* k_qs;
   uint16_t* k_d;
   uint8_t* v_qs;
   uint16_t* v_d;
   const int32_t* seg_table;
   const int32_t* start_pos;
-  int n_rows;        // n_seq * n_new * n_kv_heads
+  int n_units;       // n_seq * n_new * n_kv_heads * head_dim / 32
   int n_new;
   int n_kv_heads;
   int head_dim;
@@ -29,12 +35,26 @@ struct AppendParams {
   int v_format;
 };
 
+// max over the 32 lanes of a half-wave
+__device__ __forceinline__ float max32(float x) {
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) x = fmaxf(x, shfl_xor_f(x, m));
+  return x;
+}
+__device__ __forceinline__ int min32(int x) {
+#pragma unroll
+  for (int m = 1; m < 32; m <<= 1) x = min(x, __shfl_xor(x, m));
+  return x;
+}
+
 __global__ __launch_bounds__(256) void k_append_quant(AppendParams p) {
   const int nb = p.head_dim / kBlock;
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= p.n_rows * nb) return;
-  const int row = gid / nb;
-  const int b = gid - row * nb;
+  const int unit = gid >> 5;            // (row, block); whole half-waves share one unit
+  const int e = gid & 31;               // element inside the block
+  if (unit >= p.n_units) return;
+  const int row = unit / nb;
+  const int b = unit - row * nb;
   const int h = row % p.n_kv_heads;
   const int j = (row / p.n_kv_heads) % p.n_new;
   const int seq = row / (p.n_kv_heads * p.n_new);
@@ -42,97 +62,49 @@ __global__ __launch_bounds__(256) void k_append_quant(AppendParams p) {
   const int pos = p.start_pos[seq] + j;
   const int segj = pos / p.seg_tokens;
   const int seg = segment_of(p.seg_table, seq, p.max_segs, segj);
-  const size_t crow = ((size_t)seg * p.n_kv_heads + h) * p.seg_tokens + (pos - segj * p.seg_tokens);
+  const size_t prow = ((size_t)seg * p.n_kv_heads + h) * p.seg_tokens + (pos - segj * p.seg_tokens);
+  const size_t tile0 = prow & ~(size_t)(kTile - 1);   // first row of this token's V tile
+  const int t = (int)(prow - tile0);
 
-  float x[kBlock];
+  const size_t src = (size_t)row * p.head_dim + b * kBlock + e;
 
-  // ---- K: a = max|x|, d = fp16(a / 127), codes with the fp16 scale
+  // ---- K: a = max|x|, d = fp16(a / 127), c = clamp(rne(x / d), -127, 127)
   {
-    const float4* src = reinterpret_cast<const float4*>(p.k_new + (size_t)row * p.head_dim + b * kBlock);
-#pragma unroll
-    for (int i = 0; i < kBlock / 4; ++i) {
-      float4 v = src[i];
-      x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
-    }
-    float a = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kBlock; ++i) a = fmaxf(a, fabsf(x[i]));
+    const float x = p.k_new[src];
+    const float a = max32(fabsf(x));
     const uint16_t dbits = f32_to_half_bits(a / 127.0f);
     const float d = half_bits_to_f32(dbits);
-    uint32_t w[kBlock / 4];
-#pragma unroll
-    for (int i = 0; i < kBlock / 4; ++i) {
-      uint32_t word = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        word |= ((uint32_t)(quant_code(x[4 * i + k], d, -127.0f, 127.0f) & 0xFF)) << (8 * k);
-      w[i] = word;
-    }
-    uint4* dst = reinterpret_cast<uint4*>(p.k_qs + crow * (p.head_dim / 4) + b * (kBlock / 4));
-    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    p.k_d[crow * nb + b] = dbits;
+    p.k_qs[prow * p.head_dim + b * kBlock + e] = (uint8_t)quant_code(x, d, -127.0f, 127.0f);
+    if (e == 0) p.k_d[prow * nb + b] = dbits;
   }
 
   // ---- V
-  {
-    const float4* src = reinterpret_cast<const float4*>(p.v_new + (size_t)row * p.head_dim + b * kBlock);
-#pragma unroll
-    for (int i = 0; i < kBlock / 4; ++i) {
-      float4 v = src[i];
-      x[4 * i] = v.x; x[4 * i + 1] = v.y; x[4 * i + 2] = v.z; x[4 * i + 3] = v.w;
-    }
-    if (p.v_format == 0) {
-      // q4_0: m = first element of largest magnitude, d = fp16(m / -8),
-      // n = clamp(rne(x/d) + 8, 0, 15); byte j = n_j | n_{j+16} << 4
-      float a = -1.0f, m = 0.0f;
-#pragma unroll
-      for (int i = 0; i < kBlock; ++i) {
-        const float ax = fabsf(x[i]);
-        if (ax > a) { a = ax; m = x[i]; }
-      }
-      // fp16(m / -8) of m = +-0 is -+0.  The compiler contracts the scaling
-      // and the fp16 conversion into one fma with a +0 addend, which would
-      // turn -0 into +0, so the zero case is spelled out.
-      const uint16_t dbits = (m == 0.0f) ? (signbit(m) ? (uint16_t)0x0000 : (uint16_t)0x8000)
-                                         : f32_to_half_bits(m / -8.0f);
-      const float d = half_bits_to_f32(dbits);
-      uint32_t w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int jj = 4 * i + k;
-          const uint32_t lo = (d == 0.0f) ? 8u : (uint32_t)(quant_code(x[jj], d, -8.0f, 7.0f) + 8);
-          const uint32_t hi = (d == 0.0f) ? 8u : (uint32_t)(quant_code(x[jj + 16], d, -8.0f, 7.0f) + 8);
-          word |= (lo | (hi << 4)) << (8 * k);
-        }
-        w[i] = word;
-      }
-      uint4* dst = reinterpret_cast<uint4*>(p.v_qs + crow * (p.head_dim / 2) + b * 16);
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      p.v_d[crow * nb + b] = dbits;
-    } else {
-      float a = 0.0f;
-#pragma unroll
-      for (int i = 0; i < kBlock; ++i) a = fmaxf(a, fabsf(x[i]));
-      const uint16_t dbits = f32_to_half_bits(a / 127.0f);
-      const float d = half_bits_to_f32(dbits);
-      uint32_t w[kBlock / 4];
-#pragma unroll
-      for (int i = 0; i < kBlock / 4; ++i) {
-        uint32_t word = 0;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          word |= ((uint32_t)(quant_code(x[4 * i + k], d, -127.0f, 127.0f) & 0xFF)) << (8 * k);
-        w[i] = word;
-      }
-      uint4* dst = reinterpret_cast<uint4*>(p.v_qs + crow * p.head_dim + b * kBlock);
-      dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
-      dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-      p.v_d[crow * nb + b] = dbits;
-    }
+  const float x = p.v_new[src];
+  if (p.v_format == 0) {
+    // q4_0: m = first element of largest magnitude, d = fp16(m / -8),
+    // n = clamp(rne(x / d) + 8, 0, 15); byte j of the block = n_j | n_{j+16} << 4
+    const float ax = fabsf(x);
+    const float a = max32(ax);
+    const int first = min32(ax == a ? e : kBlock);
+    const float m = __shfl(x, ((int)__lane_id() & 32) + first);
+    // fp16(m / -8) of m = +-0 is -+0.  The compiler contracts the scaling and
+    // the fp16 conversion into one fma with a +0 addend, which would turn -0
+    // into +0, so the zero case is spelled out.
+    const uint16_t dbits = (m == 0.0f) ? (signbit(m) ? (uint16_t)0x0000 : (uint16_t)0x8000)
+                                       : f32_to_half_bits(m / -8.0f);
+    const float d = half_bits_to_f32(dbits);
+    const int n = quant_code(x, d, -8.0f, 7.0f) + 8;
+    const int n_hi = __shfl_xor(n, 16);
+    if (e < 16)
+      p.v_qs[tile0 * (p.head_dim / 2) + (size_t)(b * 16 + e) * kTile + t] = (uint8_t)(n | (n_hi << 4));
+    if (e == 0) p.v_d[tile0 * nb + b * kTile + t] = dbits;
+  } else {
+    const float a = max32(fabsf(x));
+    const uint16_t dbits = f32_to_half_bits(a / 127.0f);
+    const float d = half_bits_to_f32(dbits);
+    p.v_qs[tile0 * p.head_dim + (size_t)(b * kBlock + e) * kTile + t] =
+        (uint8_t)quant_code(x, d, -127.0f, 127.0f);
+    if (e == 0) p.v_d[tile0 * nb + b * kTile + t] = dbits;
   }
 }
 
@@ -142,20 +114,20 @@ int launch_append(const kvq_cache& c, const float* k_new, const float* v_new, in
   AppendParams p;
   p.k_new = k_new;
   p.v_new = v_new;
-  p.k_qs = c.k_qs;
+  p.k_qs = reinterpret_cast<uint8_t*>(c.k_qs);
   p.k_d = c.k_d;
   p.v_qs = c.v_qs;
   p.v_d = c.v_d;
   p.seg_table = seg_table;
   p.start_pos = start_pos;
-  p.n_rows = n_seq * n_new * c.n_kv_heads;
+  p.n_units = n_seq * n_new * c.n_kv_heads * (c.head_dim / kBlock);
   p.n_new = n_new;
   p.n_kv_heads = c.n_kv_heads;
   p.head_dim = c.head_dim;
   p.seg_tokens = c.seg_tokens;
   p.max_segs = max_segs;
   p.v_format = c.v_format;
-  const long long threads = (long long)p.n_rows * (c.head_dim / kBlock);
+  const long long threads = (long long)p.n_units * kBlock;
   const int block = 256;
   const unsigned grid = (unsigned)((threads + block - 1) / block);
   hipLaunchKernelGGL(k_append_quant, dim3(grid), dim3(block), 0, stream, p);

@@ -7,6 +7,12 @@
 namespace kvq {
 
 constexpr int kBlock = 32;   // elements per quantization block along head_dim
+constexpr int kTile = 32;    // tokens per V tile (V is stored token-interleaved per tile)
+constexpr int kRows = 16;    // MFMA rows: query tokens x query heads of one kv group, padded
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 // fp32 -> binary16 bits with the hardware conversion (round to nearest even,
 // binary16 subnormals kept).
@@ -29,7 +35,8 @@ __device__ __forceinline__ int quant_code(float x, float d, float lo, float hi) 
 
 // Cross-lane moves.  DPP controls (gfx9 encoding): quad_perm [1,0,3,2] = 0xB1
 // (lane ^ 1), quad_perm [2,3,0,1] = 0x4E (lane ^ 2), row_half_mirror = 0x141
-// (lane i <-> 7-i inside each 8), row_ror:8 = 0x128 (lane ^ 8 inside a row).
+// (lane i <-> 7-i inside each 8), row_mirror = 0x140 (lane i <-> 15-i inside
+// each 16).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
   return __builtin_bit_cast(
@@ -46,37 +53,19 @@ __device__ __forceinline__ float shfl_xor_f(float x, int mask) {
       float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, x)));
 }
 
-// Sum over the PARTS consecutive lanes that share one token (PARTS = 4 or 8);
-// every lane of the group receives the total.
-template <int PARTS>
-__device__ __forceinline__ float sum_parts(float x) {
+// Max / sum over the 16 lanes of a DPP row (lane ^ 1, ^ 2, mirror in 8, mirror in 16).
+__device__ __forceinline__ float max_row16(float x) {
+  x = fmaxf(x, dpp_f<0xB1>(x));
+  x = fmaxf(x, dpp_f<0x4E>(x));
+  x = fmaxf(x, dpp_f<0x141>(x));
+  x = fmaxf(x, dpp_f<0x140>(x));
+  return x;
+}
+__device__ __forceinline__ float sum_row16(float x) {
   x += dpp_f<0xB1>(x);
   x += dpp_f<0x4E>(x);
-  if constexpr (PARTS == 8) x += dpp_f<0x141>(x);
-  return x;
-}
-template <int PARTS>
-__device__ __forceinline__ int isum_pair(int x) {
-  static_assert(PARTS >= 2, "");
-  return x + dpp_i<0xB1>(x);
-}
-
-// Reduce over the token slots of a wave (lanes that differ in the bits above
-// log2(PARTS)); every lane receives the result.
-template <int PARTS>
-__device__ __forceinline__ float max_slots(float x) {
-  if constexpr (PARTS == 4) x = fmaxf(x, dpp_f<0x128 - 4>(x));   // row_ror:4 -> lane ^ 4 after quad max
-  x = fmaxf(x, dpp_f<0x128>(x));
-  x = fmaxf(x, shfl_xor_f(x, 16));
-  x = fmaxf(x, shfl_xor_f(x, 32));
-  return x;
-}
-template <int PARTS>
-__device__ __forceinline__ float sum_slots(float x) {
-  if constexpr (PARTS == 4) x += dpp_f<0x128 - 4>(x);
-  x += dpp_f<0x128>(x);
-  x += shfl_xor_f(x, 16);
-  x += shfl_xor_f(x, 32);
+  x += dpp_f<0x141>(x);
+  x += dpp_f<0x140>(x);
   return x;
 }
 
@@ -99,10 +88,6 @@ __device__ __forceinline__ void quantize_q_wave(const float* src, int n, int8_t*
     codes[e0 + lane] = (int8_t)quant_code(x, d, -127.0f, 127.0f);
     if ((lane & 31) == 0) scales[(e0 + lane) / kBlock] = d;
   }
-}
-
-__device__ __forceinline__ int dot4(uint32_t a, uint32_t b, int acc) {
-  return __builtin_amdgcn_sdot4((int)a, (int)b, acc, false);
 }
 
 // Segment lookup for token t of sequence `seq`.

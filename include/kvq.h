@@ -38,7 +38,7 @@ extern "C" {
 #define KVQ_ABI_VERSION 1
 #define KVQ_BLOCK 32            /* elements per quantization block along head_dim */
 #define KVQ_SEG_ALIGN 64        /* seg_tokens must be a positive multiple of this */
-#define KVQ_MAX_QTOK 16         /* largest query-token count per sequence (verify) */
+#define KVQ_MAX_QTOK 16         /* query tokens x query heads per kv head, at most */
 
 enum kvq_status {
   KVQ_OK = 0,
@@ -55,12 +55,18 @@ enum kvq_v_format {
 
 /*
  * A packed KV cache.  All four planes are device memory owned by the caller,
- * laid out [n_segs][n_kv_heads][seg_tokens][...] with one token row per line:
- *   k_qs  uint32 [..][head_dim/4]   int8 K codes, byte k of word w = element 4w+k
+ * laid out [n_segs][n_kv_heads][seg_tokens][...]:
+ *   k_qs  uint32 [..][head_dim/4]   int8 K codes of one token per row,
+ *                                   byte k of word w = element 4w+k
  *   k_d   uint16 [..][head_dim/32]  fp16 bit patterns, one per 32-block
- *   v_qs  uint8  [..][head_dim/2]   (q4_0) byte j of a block = element j | element j+16 << 4
- *         uint8  [..][head_dim]     (q8_0) int8 codes
+ *   v_qs  uint8  [..][vrow]         V payload, vrow = head_dim/2 (q4_0) or head_dim (q8_0)
  *   v_d   uint16 [..][head_dim/32]  fp16 bit patterns
+ * K is token-major.  V is token-interleaved in tiles of 32 tokens (rows 32i ..
+ * 32i+31 of a segment): inside a tile, byte k of token t's q4_0/q8_0 row is
+ * stored at byte k*32 + t and scale b of token t at scale slot b*32 + t, so the
+ * reduction axis of P.V is contiguous ("BitLLM", page 3, on matching the layout
+ * to the reduction axis).  A q4_0 row holds, per 32-block, bytes
+ * j = 0..15 = nibble(element j) | nibble(element j+16) << 4.
  * Token t of sequence i lives in segment seg_table[i*max_segs + t/seg_tokens]
  * (or segment i*max_segs + t/seg_tokens when no table is given), at row
  * t % seg_tokens.  A contiguous cache is one segment per sequence.
@@ -113,9 +119,11 @@ int kv_append_quant(const kvq_cache* cache, const float* k_new, const float* v_n
 
 /*
  * Workspace bytes attn_decode_packed needs for this shape (host only).  The
- * workspace holds per-split softmax partials; it is caller-owned device
- * memory, not read before written, and may be reused between calls on one
- * stream.
+ * workspace is caller-owned device memory holding per-split softmax partials
+ * and one split counter per (sequence, kv head).  It must be zero-filled
+ * before its first use; every completed call leaves the counters at zero, so
+ * it can be reused by later calls on the same stream without clearing.
+ * Calls that overlap in time must use different workspaces.
  */
 int attn_decode_packed_workspace_size(const kvq_cache* cache, int n_seq, int n_qtok,
                                       int n_q_heads, int max_seq_len, size_t* bytes);
@@ -134,7 +142,9 @@ int attn_decode_packed_workspace_size(const kvq_cache* cache, int n_seq, int n_q
  * int8 per 32-block with an fp32 scale (a = max|q|, d = a/127, codes as for K),
  * QK^T is summed in int32 per block and rescaled in fp32, softmax runs per
  * context split with an online maximum, V is dequantized inside the
- * weighted sum, and a second pass merges the splits.  n_qtok is 1..16.
+ * weighted sum, and the last work-group of each (sequence, kv head) merges
+ * the splits.  n_qtok * (n_q_heads / n_kv_heads) must be at most 16
+ * (KVQ_ERR_UNSUPPORTED otherwise).
  */
 int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n_seq,
                        int n_qtok, int n_q_heads, const int32_t* seg_table, int max_segs,

@@ -58,9 +58,17 @@ def gpu_rows(cache, ci: CacheInputs, i: int, tokens: np.ndarray):
     seg = ci.seg_table[i, segj] if ci.seg_table is not None else i * max_segs + segj
     row = torch.from_numpy((tokens - segj * seg_tokens).astype(np.int64)).cuda()
     segt = torch.from_numpy(seg.astype(np.int64)).cuda()
+    ntile = seg_tokens // 32
+    tile = torch.from_numpy((tokens - segj * seg_tokens).astype(np.int64) // 32).cuda()
+    slot = torch.from_numpy((tokens - segj * seg_tokens).astype(np.int64) % 32).cuda()
     out = []
-    for plane in (cache.k_qs, cache.k_d, cache.v_qs, cache.v_d):
-        x = plane[segt, :, row]                   # [n][Hkv][...]
+    for plane in (cache.k_qs, cache.k_d):          # token-major rows
+        x = plane[segt, :, row]                    # [n][Hkv][...]
+        out.append(x.permute(1, 0, 2).contiguous().cpu().numpy())
+    for plane in (cache.v_qs, cache.v_d):          # 32-token tiles, [row byte][token]
+        s_, h_, _, w_ = plane.shape
+        t5 = plane.view(s_, h_, ntile, w_, 32)
+        x = t5[segt, :, tile, :, slot]             # [n][Hkv][w]
         out.append(x.permute(1, 0, 2).contiguous().cpu().numpy())
     kq, kd, vq, vd = out
     return kq.view(np.uint32), kd.view(np.uint16), vq.view(np.uint8), vd.view(np.uint16)
@@ -97,7 +105,7 @@ def run_attention(cache, ci: CacheInputs, table, max_segs, q=None, seq_len=None,
     out = torch.empty_like(q)
     n_seq, n_qtok, n_q_heads, _ = q.shape
     ws_bytes = K.attn_decode_packed_workspace_size(cache, n_seq, n_qtok, n_q_heads, mx)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     if table is None:
         table = torch.stack([torch.arange(i * max_segs, (i + 1) * max_segs, dtype=torch.int32)
                              for i in range(n_seq)]).cuda()

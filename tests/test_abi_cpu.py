@@ -80,8 +80,9 @@ def test_bad_cache_rejected(kw, status):
 def test_bad_attention_args_rejected():
     c = _fake_cache()
     assert _attn(c, hq=12) == K.KVQ_ERR_INVALID              # not a multiple of n_kv_heads
-    assert _attn(c, hq=8 * 3) == K.KVQ_ERR_UNSUPPORTED       # group of 3 not built
+    assert _attn(c, hq=8 * 17) == K.KVQ_ERR_UNSUPPORTED      # 17 rows per kv head
     assert _attn(c, n_qtok=17) == K.KVQ_ERR_INVALID
+    assert _attn(c, n_qtok=5) == K.KVQ_ERR_UNSUPPORTED        # 5 tokens x 4 heads > 16
     assert _attn(c, max_len=2048) == K.KVQ_ERR_INVALID       # beyond max_segs * seg_tokens
     assert _attn(c, n_seq=2) == K.KVQ_ERR_INVALID            # no table and too few segments
     assert _attn(c, q=0x5008) == K.KVQ_ERR_INVALID           # misaligned

@@ -52,8 +52,9 @@ def test_append_token_by_token_equals_bulk():
         vv = H.dev(ci.v[:, t:t + 1])
         K.kv_append_quant(step, kk, vv, torch.tensor([t], dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
-    for a, b in ((bulk.k_qs, step.k_qs), (bulk.k_d, step.k_d), (bulk.v_qs, step.v_qs), (bulk.v_d, step.v_d)):
-        assert torch.equal(a[:, :, :200], b[:, :, :200])
+    toks = np.arange(200)
+    for a, b in zip(H.gpu_rows(bulk, ci, 0, toks), H.gpu_rows(step, ci, 0, toks)):
+        assert np.array_equal(a, b)
 
 
 def test_append_edge_blocks_bitexact():
@@ -63,23 +64,25 @@ def test_append_edge_blocks_bitexact():
     k = rng.standard_normal((1, n, Hkv, D)).astype(np.float32)
     k[0, 0] = 0.0
     k[0, 1, :, :32] = np.float32(-0.0)
-    k[0, 2] = (np.arange(D) % 32 - 15.5).astype(np.float32)      # ties at d = 1/8 steps
+    k[0, 2] = (np.arange(D) % 32 - 15.5).astype(np.float32)
     k[0, 3] *= np.float32(1e-6)
     k[0, 4] *= np.float32(3e3)
     k[0, 5, :, 0] = 127.0
     k[0, 5, :, 1:32] = np.arange(31, dtype=np.float32) + 0.5
+    k[0, 6, :, :32] = 5.0                    # every element ties for the largest magnitude
+    k[0, 7, :, 32:64] = -5.0
+    k[0, 7, :, 40] = 5.0
     for fmt in (O.V_Q4_0, O.V_Q8_0):
-        cache = K.PackedKVCache(Hkv, D, 64, 1, fmt)
-        K.kv_append_quant(cache, H.dev(k), H.dev(k), torch.zeros(1, dtype=torch.int32, device="cuda"))
+        spec = W.CacheSpec("edge", 1, 1, Hkv, Hkv, D, n, fmt)
+        ci = W.CacheInputs(spec, np.zeros((1, 1, Hkv, D), np.float32), k, k.copy(),
+                           np.array([n], np.int32), None, 1, 64)
+        cache, _, _ = H.build_cache(ci)
         torch.cuda.synchronize()
-        kq = cache.k_qs[0].cpu().numpy().view(np.uint32)
-        kd = cache.k_d[0].cpu().numpy().view(np.uint16)
-        vq = cache.v_qs[0].cpu().numpy()
-        vd = cache.v_d[0].cpu().numpy().view(np.uint16)
-        kw, kdd = O.encode_k(k[0].transpose(1, 0, 2))
-        vp, vdd = O.encode_v(k[0].transpose(1, 0, 2), fmt)
-        assert np.array_equal(kq, kw) and np.array_equal(kd, kdd)
-        assert np.array_equal(vq, vp) and np.array_equal(vd, vdd)
+        toks = np.arange(n)
+        got = H.gpu_rows(cache, ci, 0, toks)
+        want = H.oracle_rows(ci, 0, toks)
+        for g, w, nm in zip(got, want, ("k_qs", "k_d", "v_qs", "v_d")):
+            assert np.array_equal(g, w), (fmt, nm, np.argwhere(g != w)[:5])
 
 
 def test_append_full_size_sampled_rows():
@@ -192,12 +195,71 @@ def test_attention_shapes_and_ragged_tails(D, G, fmt, L):
     H.assert_close(got, H.oracle_attention(ci), f"D{D} G{G} f{fmt} L{L}")
 
 
+@pytest.mark.parametrize("Tq,G,causal,L,fmt", [(4, 4, True, 2000, 0), (2, 8, True, 333, 1),
+                                              (16, 1, True, 130, 0), (3, 4, False, 4100, 1),
+                                              (4, 2, True, 4, 0), (5, 3, True, 700, 1)])
+def test_attention_multi_query(Tq, G, causal, L, fmt):
+    rng = np.random.default_rng(Tq * 100 + G * 10 + L)
+    Hkv, D = 2, 128
+    spec = W.CacheSpec("mq", 1, Tq, G * Hkv, Hkv, D, L, fmt, causal=causal)
+    cap = -(-L // 64) * 64
+    ci = W.CacheInputs(spec, rng.standard_normal((1, Tq, G * Hkv, D)).astype(np.float32),
+                       (rng.standard_normal((1, L, Hkv, D)) * 1.5).astype(np.float32),
+                       rng.standard_normal((1, L, Hkv, D)).astype(np.float32),
+                       np.array([L], np.int32), None, 1, cap)
+    cache, table, max_segs = H.build_cache(ci)
+    got = H.run_attention(cache, ci, table, max_segs)
+    H.assert_close(got, H.oracle_attention(ci), f"Tq{Tq} G{G} causal{causal} L{L}")
+
+
+def test_attention_verify_small():
+    # the speculative-verify recipe (main 32/8 and draft 16/4, 4 causal query
+    # tokens) at a short context, every output checked
+    for ci in W.make_inputs("verify128k", ctx=3000):
+        _say(f"verify small {ci.spec.name}")
+        cache, table, max_segs = H.build_cache(ci)
+        got = H.run_attention(cache, ci, table, max_segs)
+        H.assert_close(got, H.oracle_attention(ci), "verify-small " + ci.spec.name)
+
+
+def test_attention_verify128k_full_size():
+    """Both caches of the verify step at 131072 tokens; the oracle checks
+    the query heads of two kv heads per cache."""
+    for ci, kvs in zip(W.make_inputs("verify128k"), ([0, 7], [1, 3])):
+        _say(f"verify full {ci.spec.name}")
+        cache, table, max_segs = H.build_cache(ci)
+        got = H.run_attention(cache, ci, table, max_segs)
+        G = ci.spec.n_q_heads // ci.spec.n_kv_heads
+        heads = [h for kv in kvs for h in range(kv * G, (kv + 1) * G)]
+        H.assert_close(got, H.oracle_attention(ci, q_heads=heads), "verify-full " + ci.spec.name)
+        del cache
+
+
 def test_attention_deterministic():
     ci = W.make_inputs("gqa8k")[0]
     cache, table, max_segs = H.build_cache(ci)
     a = H.run_attention(cache, ci, table, max_segs)
     b = H.run_attention(cache, ci, table, max_segs)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_workspace_reuse_across_shapes():
+    # counters left at zero: the same workspace serves calls of different shapes
+    ci = W.make_inputs("gqa8k", ctx=4096)[0]
+    cache, table, max_segs = H.build_cache(ci)
+    need = K.attn_decode_packed_workspace_size(cache, 1, 1, 32, 4096)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    q = H.dev(ci.q)
+    out = torch.empty_like(q)
+    ref_full = H.oracle_attention(ci)
+    for L in (4096, 1000, 4096, 77):
+        sl = torch.tensor([L], dtype=torch.int32, device="cuda")
+        K.attn_decode_packed(cache, q, out, sl, L, ci.spec.sm_scale, False, ws)
+        torch.cuda.synchronize()
+        if L == 4096:
+            H.assert_close(out.cpu().numpy(), ref_full, f"reuse L={L}")
+    counters = ws[:4 * 8].cpu().numpy().view(np.uint32)
+    assert not counters.any()
 
 
 def test_attention_errors_leave_output_untouched():
@@ -207,11 +269,11 @@ def test_attention_errors_leave_output_untouched():
     out = torch.full_like(q, 7.0)
     sl = H.dev(ci.seq_len)
     need = K.attn_decode_packed_workspace_size(cache, 1, 1, 4, 128)
-    small = torch.empty(max(need - 16, 16), dtype=torch.uint8, device="cuda")
+    small = torch.zeros(max(need - 16, 16), dtype=torch.uint8, device="cuda")
     with pytest.raises(K.KvqError) as e:
         K.attn_decode_packed(cache, q, out, sl, 128, 0.1, False, small)
     assert e.value.status == K.KVQ_ERR_WORKSPACE
-    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     with pytest.raises(K.KvqError) as e:
         K.attn_decode_packed(cache, q, out, sl, 100000, 0.1, False, ws)
     assert e.value.status == K.KVQ_ERR_INVALID
