@@ -39,8 +39,8 @@ __device__ __forceinline__ int quant_code(float x, float d, float lo, float hi) 
 // each 16).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+  return __builtin_bit_cast(float,
+                            __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
 }
 template <int CTRL>
 __device__ __forceinline__ int dpp_i(int x) {
@@ -69,25 +69,28 @@ __device__ __forceinline__ float sum_row16(float x) {
   return x;
 }
 
-// Quantize `n` (a multiple of 64) consecutive fp32 values of Q with one wave:
-// per 32-block a = max|x|, d = a / 127 kept in fp32, codes as quant_code.
+// One element of Q quantization: x is element `idx` of a row of blocks, and
+// the 32 lanes of this half-wave hold the 32 elements of its block.  Per
+// 32-block a = max|x|, d = a / 127 kept in fp32, codes as quant_code.
+__device__ __forceinline__ void quantize_q_lane(float x, int idx, int8_t* codes, float* scales) {
+  float a = fabsf(x);
+  a = fmaxf(a, shfl_xor_f(a, 1));
+  a = fmaxf(a, shfl_xor_f(a, 2));
+  a = fmaxf(a, shfl_xor_f(a, 4));
+  a = fmaxf(a, shfl_xor_f(a, 8));
+  a = fmaxf(a, shfl_xor_f(a, 16));
+  const float d = a / 127.0f;
+  codes[idx] = (int8_t)quant_code(x, d, -127.0f, 127.0f);
+  if ((idx & 31) == 0) scales[idx / kBlock] = d;
+}
+
+// Quantize `n` (a multiple of 64) consecutive fp32 values of Q with one wave.
 // Codes go to `codes` (n bytes) and scales to `scales` (n / 32 floats); both
 // may be LDS or global.  Lanes 0..31 and 32..63 each cover one block per step.
 __device__ __forceinline__ void quantize_q_wave(const float* src, int n, int8_t* codes,
                                                 float* scales) {
   const int lane = __lane_id();
-  for (int e0 = 0; e0 < n; e0 += 64) {
-    const float x = src[e0 + lane];
-    float a = fabsf(x);
-    a = fmaxf(a, shfl_xor_f(a, 1));
-    a = fmaxf(a, shfl_xor_f(a, 2));
-    a = fmaxf(a, shfl_xor_f(a, 4));
-    a = fmaxf(a, shfl_xor_f(a, 8));
-    a = fmaxf(a, shfl_xor_f(a, 16));
-    const float d = a / 127.0f;
-    codes[e0 + lane] = (int8_t)quant_code(x, d, -127.0f, 127.0f);
-    if ((lane & 31) == 0) scales[(e0 + lane) / kBlock] = d;
-  }
+  for (int e0 = 0; e0 < n; e0 += 64) quantize_q_lane(src[e0 + lane], e0 + lane, codes, scales);
 }
 
 // Segment lookup for token t of sequence `seq`.
