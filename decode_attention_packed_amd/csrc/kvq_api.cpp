@@ -66,9 +66,9 @@ SplitPlan plan_splits(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads, 
     if (chunk < kChunkAlign || chunk % kChunkAlign) chunk = 0;
   }
   if (!chunk) {
-    // Grow the chunk while at least ~2 work-groups per CU remain and the
-    // longest sequence still spreads over 8 or more of them.
-    const long long target_groups = 512;
+    // Grow the chunk while at least one work-group per CU (256 CUs) remains
+    // and the longest sequence still spreads over 8 or more of them.
+    const long long target_groups = 256;
     chunk = kChunkAlign;
     while (chunk < (1 << 20)) {
       const long long next = 2LL * chunk;

@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void k_append_quant(AppendParams p) {
   const int segj = pos / p.seg_tokens;
   const int seg = segment_of(p.seg_table, seq, p.max_segs, segj);
   const size_t prow = ((size_t)seg * p.n_kv_heads + h) * p.seg_tokens + (pos - segj * p.seg_tokens);
-  const size_t tile0 = prow & ~(size_t)(kTile - 1);   // first row of this token's V tile
+  const size_t tile0 = prow & ~(size_t)(kTile - 1);   // first row of this token's 32-token tile
   const int t = (int)(prow - tile0);
 
   const size_t src = (size_t)row * p.head_dim + b * kBlock + e;
@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void k_append_quant(AppendParams p) {
     const uint16_t dbits = f32_to_half_bits(a / 127.0f);
     const float d = half_bits_to_f32(dbits);
     p.k_qs[prow * p.head_dim + b * kBlock + e] = (uint8_t)quant_code(x, d, -127.0f, 127.0f);
-    if (e == 0) p.k_d[prow * nb + b] = dbits;
+    if (e == 0) p.k_d[tile0 * nb + b * kTile + t] = dbits;
   }
 
   // ---- V

@@ -1,31 +1,45 @@
 // Split-K decode attention over the packed cache (MFMA path).
 //
-// One work-group of four waves owns one (sequence, kv head, context chunk)
-// and all query rows of that kv group: up to 16 rows = query tokens x query
-// heads, so grouped query heads (and the verify step's query tokens) share
-// every K/V byte loaded.  Waves take 32-token tiles of the chunk in turn.
+// One work-group of eight waves (one per CU) owns one (sequence, kv head,
+// context chunk) and all query rows of that kv group (query tokens x query
+// heads, at most 16), so grouped query heads and the verify step's query
+// tokens share every K/V byte loaded.  The chunk's 32-token tiles are handed
+// out to the waves in order from an LDS counter, so waves that run ahead take
+// more of them.
 //
 // Memory: each wave streams its tiles through a ring of LDS slots with
 // direct global->LDS loads (16 bytes per lane), up to two tiles ahead of the
-// one it is working on, so every CU keeps ~100 KB of K/V in flight without
-// holding it in registers.  Chunks are XOR-swizzled on their way into LDS so
-// the 8-byte operand reads below spread over the banks.
+// one it is working on, so a CU keeps ~130 KB of K/V in flight without
+// holding it in registers.  K rows are XOR-swizzled on their way into LDS so
+// the 8-byte operand reads spread over the banks.
 //
-//   QK^T   v_mfma_i32_16x16x32_i8, one MFMA per 32-block and 16 tokens, so
-//          each block keeps its own int32 dot sum (page 1: int8 K and Q go
-//          straight into the integer dot); the sums are rescaled in fp32 by
-//          d_q * d_k and summed over blocks, in the log2 domain.
-//   softmax running maximum per row, updated once per tile; the
-//          accumulators are rescaled only when it grows.
-//   P.V    v_mfma_f32_16x16x32_f16.  V tiles are stored token-interleaved
-//          (32 tokens per tile, "BitLLM" page 3: the layout follows the
-//          reduction axis, which is T for S.V), so one 8-byte read per lane is
-//          8 tokens of one nibble pair = one MFMA B operand.  Nibbles become
-//          exact fp16 integers (n - 8) with a byte permute and one packed f16
-//          add; A = p * d_v is split into fp16 hi + lo so the weights keep
-//          about 22 bits.
+// Two tile bodies share that machinery.
 //
-// The four waves merge through LDS and the group writes one unnormalized
+// Column layout (rows x blocks <= 16: single-token decode with up to 4
+// grouped heads at head_dim 128, 8 at 64).  The 16 MFMA columns are the
+// (query row, quant block) pairs.
+//   QK^T   v_mfma_i32_16x16x32_i8 with A = K rows (16 tokens) and B = the Q
+//          codes of block b placed only in the columns of block b, so one
+//          accumulator collects every block's int32 dot in its own column
+//          (page 1: int8 K and Q go straight into the integer dot).  Each
+//          column scales its dots by d_q * d_k and a DPP butterfly over the
+//          block columns of a row adds them up: every lane then holds the
+//          scores of 8 consecutive tokens of one row, with no padding rows.
+//   softmax the running maximum is checked lane by lane; the cross-lane
+//          reduction and the rescale of the accumulators only run when a
+//          score exceeds it.
+//   P.V    computed transposed, v_mfma_f32_16x16x32_f16 with A = 16 dims of
+//          V codes (exact fp16 integers from a byte permute and one packed
+//          f16 add) and B = p * d_v of the column's block, split into fp16
+//          hi + lo (about 22 bits).  V tiles are stored token-interleaved
+//          ("BitLLM" page 3: the layout follows the reduction axis, T for
+//          S.V), so one 8-byte read is 8 tokens of one dim.
+//
+// Row layout (larger groups, e.g. 4 query tokens x 4 heads): the 16 MFMA
+// rows are query rows; the per-block dots come from one MFMA per block, P
+// goes through LDS into the A operand and B is the dequantized V.
+//
+// The eight waves merge through LDS and the group writes one unnormalized
 // partial (m, l, o) per row.  The last group to finish a (sequence, kv head)
 // -- counted with a device-scope atomic in the workspace -- merges all of
 // its partials and writes the output rows, then resets the counter.
@@ -34,9 +48,13 @@
 #include "kvq_launch.h"
 #include "kvq_qk.h"
 
+#include <type_traits>
+
 namespace kvq {
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                  // one work-group fills a CU (two waves per SIMD)
+constexpr int kThreads = kWaves * 64;
+constexpr int kLdsBudget = 163840 - 512;   // LDS of one work-group, less the small shared words
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
@@ -79,33 +97,37 @@ struct Slot {
   static constexpr int DV_OFF = DK_OFF + SBYTES;
   static constexpr int BYTES = DV_OFF + SBYTES;
   static constexpr int CPR = D / 16;                 // 16-byte chunks per K row
-  static constexpr int PBYTES = kRows * (kTile + 4) * 4;   // padded P staging tile
+  static constexpr int PBYTES = kRows * (kTile + 4) * 4;   // padded P staging tile (row layout)
   static constexpr bool P_IN_K = PBYTES <= KBYTES;   // P can reuse the K area
-  // three slots per wave where two groups of four waves still fit in a CU
-  static constexpr int NSLOT = (3 * BYTES * kWaves <= 81920) ? 3 : 2;
+  static constexpr int PBUF = P_IN_K ? 0 : kWaves * PBYTES;   // row layout only
+  // three slots per wave where they fit in the CU's LDS, else two
+  static constexpr int NSLOT = (3 * BYTES * kWaves + PBUF <= kLdsBudget) ? 3 : 2;
+  static constexpr int QSTAGE = 1024;                // fp32 Q rows of one wave (at most 1 KB)
+  static constexpr int LPT = KBYTES / 1024 + VBYTES / 1024 + (SBYTES == 256 ? 2 : 1);   // loads per tile
   static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "whole 1 KB load steps");
+  static_assert(kRows / kWaves * D * 4 <= QSTAGE && QSTAGE + kRows * D + kRows * NB * 4 <= BYTES,
+                "Q staging does not fit a slot");
+  static_assert(NSLOT * BYTES * kWaves + PBUF <= kLdsBudget, "ring does not fit the LDS");
 };
 
 // Direct global->LDS loads (lane l's bytes land at lds + size * l for the
 // 16- and 4-byte forms used here; the sub-dword forms keep a 4-byte lane
-// stride, so they are not used) issued
-// from inline assembly: the compiler cannot tell which LDS bytes such a load
-// writes and would wait for all of them before every LDS read, which undoes
-// the ring.  The kernel counts these loads itself with vmcnt.  The address
-// is a uniform base plus a per-lane 32-bit offset.
+// stride, so they are not used) issued from inline assembly: the compiler
+// cannot tell which LDS bytes such a load writes and would wait for all of
+// them before every LDS read, which undoes the ring.  The kernels count these
+// loads themselves with vmcnt.  The address is a uniform base plus a
+// per-lane 32-bit offset, or a per-lane 64-bit address.
 template <int SIZE>
 __device__ __forceinline__ void dma(const void* sbase, uint32_t voff, uint32_t lds) {
+  static_assert(SIZE == 16 || SIZE == 4, "16 or 4 bytes per lane");
   if constexpr (SIZE == 16) {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  ::"v"(voff), "s"(sbase), "s"(lds) : "memory");
-  } else if constexpr (SIZE == 4) {
+  } else {
     asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
                  ::"v"(voff), "s"(sbase), "s"(lds) : "memory");
-  } else {
-    static_assert(SIZE == 16 || SIZE == 4, "16 or 4 bytes per lane");
   }
 }
-// The same with a full per-lane 64-bit address.
 __device__ __forceinline__ void dma16_v(const void* vaddr, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                ::"v"(vaddr), "s"(lds) : "memory");
@@ -124,38 +146,60 @@ __device__ __forceinline__ int load_uniform(const int32_t* ptr) {
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
-// Per-lane byte offsets of one tile's loads inside its global rows; the
-// swizzle repeats every 1 KB, so every 1 KB step of a tile uses the same.
+// Per-lane byte offsets of one tile's loads inside its global rows.  The K
+// swizzle and the V chunk order repeat every 1 KB.
+template <int D, int VF>
 struct TileLane {
-  uint32_t k, v, s;
+  uint32_t k[Slot<D, VF>::KBYTES / 1024];
+  uint32_t v[Slot<D, VF>::VBYTES / 1024];
+  uint32_t s;
 };
 template <int D, int VF>
-__device__ __forceinline__ TileLane tile_lane_offsets(int lane) {
+__device__ __forceinline__ TileLane<D, VF> tile_lane_offsets(int lane) {
   using S = Slot<D, VF>;
+  TileLane<D, VF> t;
   const int r = lane / S::CPR;
   const int q = (lane % S::CPR) ^ (r % S::CPR);
   const int R = lane >> 1;
   const int c = (lane & 1) ^ ((R >> 2) & 1);
-  return {(uint32_t)(r * D + 16 * q), (uint32_t)(R * 32 + 16 * c), (uint32_t)(4 * (lane % (S::SBYTES / 4)))};
+#pragma unroll
+  for (int n = 0; n < S::KBYTES / 1024; ++n) t.k[n] = (uint32_t)(r * D + 16 * q + 1024 * n);
+#pragma unroll
+  for (int n = 0; n < S::VBYTES / 1024; ++n) t.v[n] = (uint32_t)(R * 32 + 16 * c + 1024 * n);
+  t.s = (uint32_t)(4 * (lane % (S::SBYTES / 4)));
+  return t;
 }
+
+// Segment of the tiles a wave is loading: looked up again only when a tile
+// leaves the cached segment (tiles of one wave only move forward).
+struct TileCursor {
+  int seg_hi;       // first token past the cached segment
+  long long base;   // global row of token t is base + t inside it
+};
 
 // Issue the loads of one tile (32 tokens starting at t0) into a ring slot.
 // K rows (CPR chunks) land at chunk r*CPR + (q ^ (r % CPR)); V rows (two
-// chunks) at R*2 + (c ^ ((R >> 2) & 1)); scales as they are.
+// chunks) at R*2 + (c ^ ((R >> 2) & 1)); scale planes as they are.
 template <int D, int VF>
 __device__ __forceinline__ void issue_tile(const AttnParams& p, int seq, int kvh, int t0,
-                                           uint32_t slot, const TileLane& tl) {
+                                           uint32_t slot, const TileLane<D, VF>& tl,
+                                           TileCursor& cur) {
   using S = Slot<D, VF>;
-  const int segj = __builtin_amdgcn_readfirstlane(t0 / p.seg_tokens);
-  const int seg = p.seg_table ? load_uniform(p.seg_table + (seq * p.max_segs + segj))
-                              : seq * p.max_segs + segj;
-  const size_t row0 = ((size_t)seg * p.n_kv_heads + kvh) * p.seg_tokens + (t0 - segj * p.seg_tokens);
+  if (t0 >= cur.seg_hi) {
+    const int segj = __builtin_amdgcn_readfirstlane(t0 / p.seg_tokens);
+    const int seg = p.seg_table ? load_uniform(p.seg_table + (seq * p.max_segs + segj))
+                                : seq * p.max_segs + segj;
+    const int lo = segj * p.seg_tokens;
+    cur.seg_hi = lo + p.seg_tokens;
+    cur.base = ((long long)seg * p.n_kv_heads + kvh) * p.seg_tokens - lo;
+  }
+  const long long row0 = cur.base + t0;
   const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.k_qs) + row0 * D;
 #pragma unroll
-  for (int n = 0; n < S::KBYTES / 1024; ++n) dma<16>(kg + 1024 * n, tl.k, slot + S::K_OFF + 1024 * n);
+  for (int n = 0; n < S::KBYTES / 1024; ++n) dma<16>(kg, tl.k[n], slot + S::K_OFF + 1024 * n);
   const uint8_t* vg = p.v_qs + row0 * S::VROW;
 #pragma unroll
-  for (int n = 0; n < S::VBYTES / 1024; ++n) dma<16>(vg + 1024 * n, tl.v, slot + S::V_OFF + 1024 * n);
+  for (int n = 0; n < S::VBYTES / 1024; ++n) dma<16>(vg, tl.v[n], slot + S::V_OFF + 1024 * n);
   const uint8_t* kdg = reinterpret_cast<const uint8_t*>(p.k_d) + row0 * S::NB * 2;
   const uint8_t* vdg = reinterpret_cast<const uint8_t*>(p.v_d) + row0 * S::NB * 2;
   if constexpr (S::SBYTES == 256) {
@@ -163,16 +207,141 @@ __device__ __forceinline__ void issue_tile(const AttnParams& p, int seq, int kvh
     dma<4>(vdg, tl.s, slot + S::DV_OFF);
   } else {
     // 128-byte planes: one load, lanes 0-31 K scales, lanes 32-63 V scales
-    // (DV_OFF directly follows DK_OFF)
     static_assert(S::SBYTES == 128 && S::DV_OFF == S::DK_OFF + 128, "scale planes");
     dma4_v((__lane_id() < 32 ? kdg : vdg) + tl.s, slot + S::DK_OFF);
   }
 }
 
-// VMEM instructions issue_tile emits per tile.
+// Wait until at most `pending` tiles' loads of this wave are still in flight
+// (vmcnt counts the wave's outstanding loads; each tile issues L of them).
+template <int L>
+__device__ __forceinline__ void wait_tiles(int pending) {
+  if (pending >= 2) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L) : "memory");
+  } else if (pending == 1) {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  }
+}
+
+// Tiles of a work-group's chunk are handed out in order: the first two of
+// each wave statically (wave w: tiles w and w + kWaves), the rest from an LDS
+// counter, so a wave that runs ahead takes more tiles.  One lane takes the
+// next index; the result is uniform.
+__device__ __forceinline__ int grab_tile(int* s_next, int c0) {
+  int i = 0;
+  if (__lane_id() == 0)
+    i = __hip_atomic_fetch_add(s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return c0 + kTile * __builtin_amdgcn_readfirstlane(i);
+}
+
+// A wave's tiles in flight: `cur` is the next one to process, `n1` was
+// issued after it, `g` is taken from the counter but not issued yet.  Tile
+// starts only grow, so once one is past the chunk end all later ones are.
+struct TileQueue {
+  int cur, n1, g;
+};
+
+// One step of a wave's ring: refill and wait as the slot count allows, then
+// run `body` on the tile in slot SLOT (a compile-time slot, so LDS offsets
+// become immediates).  Returns false once the wave's tiles are done.
+template <int D, int VF, int SLOT, class Body>
+__device__ __forceinline__ bool ring_step(const AttnParams& p, int seq, int kvh, int c0, int c1,
+                                          int* s_next, uint32_t ring_lds, const TileLane<D, VF>& tl,
+                                          TileCursor& cur, TileQueue& q, Body& body) {
+  using S = Slot<D, VF>;
+  if (q.cur >= c1) return false;
+  if constexpr (S::NSLOT == 3) {
+    // the grabbed tile goes into the slot freed last step
+    const int n2 = q.g;
+    if (n2 < c1) issue_tile<D, VF>(p, seq, kvh, n2, ring_lds + ((SLOT + 2) % 3) * S::BYTES, tl, cur);
+    q.g = grab_tile(s_next, c0);
+    wait_tiles<S::LPT>((q.n1 < c1) + (n2 < c1));
+    body(std::integral_constant<int, SLOT>{}, q.cur);
+    q.cur = q.n1;
+    q.n1 = n2;
+  } else {
+    wait_tiles<S::LPT>(q.n1 < c1);
+    body(std::integral_constant<int, SLOT>{}, q.cur);
+    if (q.g < c1) issue_tile<D, VF>(p, seq, kvh, q.g, ring_lds + SLOT * S::BYTES, tl, cur);
+    q.cur = q.n1;
+    q.n1 = q.g;
+    q.g = grab_tile(s_next, c0);
+  }
+  return true;
+}
+
+// Run a wave's ring to the end.  On entry tile q.cur sits in slot 0 and
+// q.n1 in slot 1 (both issued or past the end), and q.g is taken.
+template <int D, int VF, class Body>
+__device__ __forceinline__ void run_ring(const AttnParams& p, int seq, int kvh, int c0, int c1,
+                                         int* s_next, uint32_t ring_lds, const TileLane<D, VF>& tl,
+                                         TileCursor& cur, TileQueue& q, Body& body) {
+  if constexpr (Slot<D, VF>::NSLOT == 3) {
+    while (ring_step<D, VF, 0>(p, seq, kvh, c0, c1, s_next, ring_lds, tl, cur, q, body) &&
+           ring_step<D, VF, 1>(p, seq, kvh, c0, c1, s_next, ring_lds, tl, cur, q, body) &&
+           ring_step<D, VF, 2>(p, seq, kvh, c0, c1, s_next, ring_lds, tl, cur, q, body)) {
+    }
+  } else {
+    while (ring_step<D, VF, 0>(p, seq, kvh, c0, c1, s_next, ring_lds, tl, cur, q, body) &&
+           ring_step<D, VF, 1>(p, seq, kvh, c0, c1, s_next, ring_lds, tl, cur, q, body)) {
+    }
+  }
+}
+
+// Common prologue: this wave's Q rows (wave, wave + kWaves) go to its last
+// slot as fp32 ahead of its first tiles, so waiting for them leaves the tiles
+// in flight; then they are quantized (a = max|q|, d = a / 127 in fp32) into
+// codes and scales shared through wave 0's last slot.  Rows past `rows` load
+// row 0 and quantize as zeros.  Issues the wave's static tiles (q.cur, and
+// q.n1 when three slots allow it) and returns after the barrier that
+// publishes the codes.
 template <int D, int VF>
-constexpr int loads_per_tile() {
-  return Slot<D, VF>::KBYTES / 1024 + Slot<D, VF>::VBYTES / 1024 + (Slot<D, VF>::SBYTES == 256 ? 2 : 1);
+__device__ __forceinline__ void prologue(const AttnParams& p, uint8_t* s_lds, int seq, int kvh,
+                                         int wave, int c1, const TileLane<D, VF>& tl,
+                                         TileCursor& cur, const TileQueue& q, int8_t*& s_qc,
+                                         float*& s_qd) {
+  using S = Slot<D, VF>;
+  constexpr int NB = D / kBlock;
+  constexpr int NSLOT = S::NSLOT;
+  constexpr int RPW = kRows / kWaves;   // Q rows per wave
+  constexpr int PIECES = RPW * D / 4;   // 16-byte pieces of them
+  static_assert(PIECES <= 64, "one load per wave");
+  const int lane = __lane_id();
+  const int R = p.rows, G = p.group;
+  uint8_t* ring = s_lds + wave * NSLOT * S::BYTES;
+  const uint32_t ring_lds = lds_addr(ring);
+  {
+    // lanes past PIECES repeat the first pieces into the unused half
+    const int pc = lane % PIECES;
+    const int r = wave + kWaves * (pc / (D / 4));
+    const int rr = r < R ? r : 0;
+    const float* src = p.q + (((size_t)seq * p.n_qtok + rr / G) * p.n_q_heads + kvh * G + rr % G) * D +
+                       4 * (pc % (D / 4));
+    dma16_v(src, ring_lds + (NSLOT - 1) * S::BYTES);
+  }
+  const int n_pro = (q.cur < c1) + (NSLOT == 3 && q.n1 < c1);
+  if (q.cur < c1) issue_tile<D, VF>(p, seq, kvh, q.cur, ring_lds, tl, cur);
+  if (NSLOT == 3 && q.n1 < c1) issue_tile<D, VF>(p, seq, kvh, q.n1, ring_lds + S::BYTES, tl, cur);
+  wait_tiles<S::LPT>(n_pro);
+
+  const float* s_qf = reinterpret_cast<const float*>(ring + (NSLOT - 1) * S::BYTES);
+  s_qc = reinterpret_cast<int8_t*>(s_lds + (NSLOT - 1) * S::BYTES + S::QSTAGE);
+  s_qd = reinterpret_cast<float*>(s_lds + (NSLOT - 1) * S::BYTES + S::QSTAGE + kRows * D);
+  float qv[RPW][D / 64];
+#pragma unroll
+  for (int k = 0; k < RPW; ++k)
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e)
+      qv[k][e] = wave + kWaves * k < R ? s_qf[k * D + 64 * e + lane] : 0.0f;
+#pragma unroll
+  for (int k = 0; k < RPW; ++k) {
+    const int r = wave + kWaves * k;
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) quantize_q_lane(qv[k][e], 64 * e + lane, s_qc + r * D, s_qd + r * NB);
+  }
+  __syncthreads();
 }
 
 // Four bytes -> two fp16 pairs (1024 + byte) placed as [b0, b1] and [b2, b3].
@@ -208,6 +377,175 @@ __device__ __forceinline__ void split_f16_pair(float p0, float p1, uint32_t dpai
       "v_fma_mixhi_f16 %1, %3, %4, -%0 op_sel:[0,1,1] op_sel_hi:[0,1,1]"
       : "=&v"(hi), "=&v"(lo)
       : "v"(p0), "v"(p1), "v"(dpair));
+}
+
+// Publish this work-group's partial and, in the last work-group of the
+// (sequence, kv head), merge every split into the output rows.  On entry
+// s_buf holds each wave's unnormalized rows ([wave][16][D]) followed by their
+// maxima and sums ([wave][16] each), and the work-group is synchronized.  A
+// sequence with a single split writes its rows directly.
+template <int D, int LDS_BYTES>
+__device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, int* s_last, int seq,
+                                             int kvh, int split, int n_split_seq) {
+  constexpr int kBatch = 16;                              // partial loads in flight per thread
+  static_assert(kMaxSplits * kRows * 4 + 16 * kThreads <= LDS_BYTES,
+                "split merge does not fit the LDS buffer");
+  static_assert(kRows * D / 4 <= kThreads, "one thread per output column at least");
+  const int tid = threadIdx.x;
+  const int R = p.rows, G = p.group;
+  float* s_m = s_buf + kWaves * kRows * D;
+  float* s_l = s_m + kWaves * kRows;
+  auto out_row = [&](int r) {
+    return p.out + (((size_t)seq * p.n_qtok + r / G) * p.n_q_heads + kvh * G + r % G) * D;
+  };
+
+  // ---- merge the waves: one (m, l, o) per row
+  // Partials go out with agent-scope stores (write-through, coherent across
+  // XCDs once complete), so publishing needs only a wait for the stores and
+  // the counter increment, not a write-back of the whole L2.
+  const bool single = n_split_seq == 1;
+  const size_t pbase = ((size_t)seq * p.n_kv_heads + kvh) * p.n_split;
+  for (int e = tid; e < R * D; e += kThreads) {
+    const int r = e / D;
+    float M = s_m[r];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w * kRows + r]);
+    float o = 0.0f, l = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float a = __builtin_amdgcn_exp2f(s_m[w * kRows + r] - M);
+      o = fmaf(a, s_buf[(w * kRows + r) * D + (e - r * D)], o);
+      l = fmaf(a, s_l[w * kRows + r], l);
+    }
+    if (single) {
+      out_row(r)[e - r * D] = o / l;
+      continue;
+    }
+    __hip_atomic_store(&p.part_o[((pbase + split) * R) * D + e], o, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    if (e - r * D == 0) {
+      __hip_atomic_store(&p.part_ml[((pbase + split) * R + r) * 2], M, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&p.part_ml[((pbase + split) * R + r) * 2 + 1], l, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (single) return;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned done = __hip_atomic_fetch_add(&p.counters[(size_t)seq * p.n_kv_heads + kvh], 1u,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = (done == (unsigned)(n_split_seq - 1));
+  }
+  __syncthreads();
+  if (!*s_last) return;
+  // The last group of this (sequence, kv head): drop stale cached lines, then
+  // merge the partials of every split.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  static_assert(kMaxSplits <= 64, "one lane per split");
+  const int nsp = n_split_seq;
+  float* sw = s_buf;                                    // [nsp][R] split weights
+  float4* red = reinterpret_cast<float4*>(sw + kMaxSplits * kRows);   // [tpc][cols]
+  const int cols = R * D / 4;              // float4 columns of the output rows
+  const int tpc = kThreads / cols;         // threads per column
+  const int c = tid % cols, part = tid / cols;
+  const bool active = part < tpc;
+  const int r = (4 * c) / D;
+  const float* ob = p.part_o + (pbase * R) * D + 4 * c;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  // split maxima and sums first (wave w takes rows w, w + kWaves, one lane
+  // per split), then the first batch of partial outputs, all in flight at once
+  constexpr int kRowsPerWave = kRows / kWaves;
+  float2 ml[kRowsPerWave];
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) {
+    const int rr = wave + kWaves * k;
+    ml[k] = (float2){-INFINITY, 0.0f};
+    if (rr < R && lane < nsp)
+      ml[k] = *reinterpret_cast<const float2*>(p.part_ml + ((pbase + lane) * R + rr) * 2);
+  }
+  float4 v[kBatch];
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int sp = part + tpc * k;
+    if (active && sp < nsp) v[k] = *reinterpret_cast<const float4*>(ob + (size_t)sp * R * D);
+  }
+  // weights exp2(m_s - M) / sum_s exp2(m_s - M) l_s
+#pragma unroll
+  for (int k = 0; k < kRowsPerWave; ++k) {
+    const int rr = wave + kWaves * k;
+    if (rr >= R) break;
+    float M = ml[k].x;
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) M = fmaxf(M, shfl_xor_f(M, sh));
+    const float e = lane < nsp ? __builtin_amdgcn_exp2f(ml[k].x - M) : 0.0f;
+    float den = e * ml[k].y;
+#pragma unroll
+    for (int sh = 1; sh < 64; sh <<= 1) den += shfl_xor_f(den, sh);
+    if (lane < nsp) sw[lane * R + rr] = e / den;
+  }
+  __syncthreads();
+
+  float4 a = {0.0f, 0.0f, 0.0f, 0.0f};
+  auto add = [&](float w, const float4& x) {
+    a.x = fmaf(w, x.x, a.x);
+    a.y = fmaf(w, x.y, a.y);
+    a.z = fmaf(w, x.z, a.z);
+    a.w = fmaf(w, x.w, a.w);
+  };
+#pragma unroll
+  for (int k = 0; k < kBatch; ++k) {
+    const int sp = part + tpc * k;
+    if (active && sp < nsp) add(sw[sp * R + r], v[k]);
+  }
+  // more splits than one batch covers (large row groups): further batches
+  for (int sp0 = part + tpc * kBatch; active && sp0 < nsp; sp0 += tpc * kBatch) {
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int sp = sp0 + tpc * k;
+      if (sp < nsp) v[k] = *reinterpret_cast<const float4*>(ob + (size_t)sp * R * D);
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      const int sp = sp0 + tpc * k;
+      if (sp < nsp) add(sw[sp * R + r], v[k]);
+    }
+  }
+  if (active) red[part * cols + c] = a;
+  __syncthreads();
+  for (int cc = tid; cc < cols; cc += kThreads) {
+    float4 o = red[cc];
+    for (int pp = 1; pp < tpc; ++pp) {
+      const float4 b = red[pp * cols + cc];
+      o.x += b.x;
+      o.y += b.y;
+      o.z += b.z;
+      o.w += b.w;
+    }
+    const int rr = (4 * cc) / D;
+    *reinterpret_cast<float4*>(out_row(rr) + (4 * cc - rr * D)) = o;
+  }
+  if (tid == 0)
+    __hip_atomic_store(&p.counters[(size_t)seq * p.n_kv_heads + kvh], 0u, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Row layout
+// ---------------------------------------------------------------------------
+
+// wq * fp16 half (0 = low, 1 = high) of `pair`, in fp32 with one rounding.
+template <int HI>
+__device__ __forceinline__ float mul_f32_f16(float wq, uint32_t pair) {
+  float r;
+  if constexpr (HI)
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(wq), "v"(pair));
+  else
+    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(wq), "v"(pair));
+  return r;
 }
 
 // Running state of one wave: output tiles (rows 4*(lane/16)+i, dims
@@ -247,18 +585,9 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
       kb[b] = *reinterpret_cast<const long*>(slot + S::K_OFF + (r * S::CPR + (q ^ (r % S::CPR))) * 16 +
                                              8 * (grp & 1));
     }
-    _Float16 dk[NB];
-    if constexpr (NB == 4) {
-      const uint2 w = *reinterpret_cast<const uint2*>(slot + S::DK_OFF + r * 8);
-      dk[0] = __builtin_bit_cast(_Float16, (uint16_t)w.x);
-      dk[1] = __builtin_bit_cast(_Float16, (uint16_t)(w.x >> 16));
-      dk[2] = __builtin_bit_cast(_Float16, (uint16_t)w.y);
-      dk[3] = __builtin_bit_cast(_Float16, (uint16_t)(w.y >> 16));
-    } else {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(slot + S::DK_OFF + r * 4);
-      dk[0] = __builtin_bit_cast(_Float16, (uint16_t)w);
-      dk[1] = __builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-    }
+    _Float16 dk[NB];   // scale b of token r sits at slot b*32 + r
+#pragma unroll
+    for (int b = 0; b < NB; ++b) dk[b] = reinterpret_cast<const _Float16*>(slot + S::DK_OFF)[b * kTile + r];
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[h][i] = 0.0f;
 #pragma unroll
@@ -368,97 +697,39 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
   __builtin_amdgcn_wave_barrier();
 }
 
-// Wait until at most `pending` tiles' loads of this wave are still in flight
-// (vmcnt counts the wave's outstanding loads; each tile issues L of them).
-template <int L>
-__device__ __forceinline__ void wait_tiles(int pending) {
-  if (pending >= 2) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * L) : "memory");
-  } else if (pending == 1) {
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(L) : "memory");
-  } else {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  }
-}
-
 template <int D, int VF>
-__global__ __launch_bounds__(256) void k_attn_split(AttnParams p) {
+__global__ __launch_bounds__(kThreads) void k_attn_rows(AttnParams p) {
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
   constexpr int NT = D / 16;
-  constexpr int NSLOT = S::NSLOT;
-  constexpr int LPT = loads_per_tile<D, VF>();
-  constexpr int RING = kWaves * NSLOT * S::BYTES + (S::P_IN_K ? 0 : kWaves * S::PBYTES);
+  constexpr int RING = kWaves * S::NSLOT * S::BYTES + S::PBUF;
   constexpr int MERGE = kWaves * kRows * D * 4 + 2 * kWaves * kRows * 4;
   constexpr int LDS_BYTES = RING > MERGE ? RING : MERGE;
-  static_assert(2 * kMaxSplits * kRows * 4 + 16 * (kRows * D / 4 > 256 ? kRows * D / 4 : 256) <=
-                    LDS_BYTES, "split merge does not fit the LDS buffer");
-  static_assert(kRows / kWaves * D * 4 + kRows * D + kRows * NB * 4 <= S::BYTES,
-                "Q staging does not fit a slot");
 
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   __shared__ int s_last;
+  __shared__ int s_next;   // next dynamically handed-out tile of the chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar addressing
-  const int col = lane & 15;
-  const int grp = lane >> 4;
-  const int split = blockIdx.x;
-  const int kvh = blockIdx.y;
-  const int seq = blockIdx.z;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
   const int L = p.seq_len[seq];
   const int n_split_seq = (L + p.chunk - 1) / p.chunk;
-  if (split >= n_split_seq) return;               // nothing of this sequence here
+  if (split >= n_split_seq) return;
   const int c0 = split * p.chunk;
   const int c1 = min(c0 + p.chunk, L);
-  const int R = p.rows;
-  const int G = p.group;
+  const int R = p.rows, G = p.group;
+  const TileLane<D, VF> tl = tile_lane_offsets<D, VF>(lane);
+  TileCursor cur = {-1, 0};
+  TileQueue tq = {c0 + kTile * wave, c0 + kTile * (wave + kWaves), 0};
+  const uint32_t ring_lds = lds_addr(s_lds + wave * S::NSLOT * S::BYTES);
+  if (tid == 0) s_next = 2 * kWaves;
 
-  uint8_t* ring = s_lds + wave * NSLOT * S::BYTES;
-  const uint32_t ring_lds = lds_addr(ring);
-  float* pbuf = reinterpret_cast<float*>(s_lds + kWaves * NSLOT * S::BYTES + wave * S::PBYTES);
-  constexpr int kStride = kTile * kWaves;
-  const int t_first = c0 + kTile * wave;
-  const TileLane tl = tile_lane_offsets<D, VF>(lane);
-
-  // Q: this wave's rows (wave, wave + 4, ...) go to its last slot as fp32,
-  // ahead of the first tiles, so the wait for them leaves the tiles in flight.
-  // Rows past R load row 0 and quantize as zeros.
-  constexpr int QLANES = D / 4;   // 16-byte pieces per fp32 row
-#pragma unroll
-  for (int j = 0; j < D / 64; ++j) {
-    const int k = (64 * j + lane) / QLANES;
-    const int r = wave + kWaves * k;
-    const int rr = r < R ? r : 0;
-    const float* src = p.q + (((size_t)seq * p.n_qtok + rr / G) * p.n_q_heads + kvh * G + rr % G) * D +
-                       4 * ((64 * j + lane) % QLANES);
-    dma16_v(src, ring_lds + (NSLOT - 1) * S::BYTES + 1024 * j);
-  }
-  // the first tiles go to slots 0 and 1 while Q is quantized
-  const int n_pro = t_first >= c1 ? 0 : (NSLOT == 3 && t_first + kStride < c1 ? 2 : 1);
-  if (n_pro >= 1) issue_tile<D, VF>(p, seq, kvh, t_first, ring_lds, tl);
-  if (n_pro >= 2) issue_tile<D, VF>(p, seq, kvh, t_first + kStride, ring_lds + S::BYTES, tl);
-  wait_tiles<LPT>(n_pro);
-
-  // Q codes and scales are shared through wave 0's last slot, after its fp32
-  // staging; that slot is only refilled once every wave has read them.
-  const float* s_qf = reinterpret_cast<const float*>(ring + (NSLOT - 1) * S::BYTES);
-  int8_t* s_qc = reinterpret_cast<int8_t*>(s_lds + (NSLOT - 1) * S::BYTES + kRows / kWaves * D * 4);
-  float* s_qd = reinterpret_cast<float*>(s_lds + (NSLOT - 1) * S::BYTES + kRows / kWaves * D * 4 + kRows * D);
-  float qv[kRows / kWaves][D / 64];
-#pragma unroll
-  for (int k = 0; k < kRows / kWaves; ++k)
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e)
-      qv[k][e] = wave + kWaves * k < R ? s_qf[k * D + 64 * e + lane] : 0.0f;
-#pragma unroll
-  for (int k = 0; k < kRows / kWaves; ++k) {
-    const int r = wave + kWaves * k;
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) quantize_q_lane(qv[k][e], 64 * e + lane, s_qc + r * D, s_qd + r * NB);
-  }
-  __syncthreads();
+  int8_t* s_qc;
+  float* s_qd;
+  prologue<D, VF>(p, s_lds, seq, kvh, wave, c1, tl, cur, tq, s_qc, s_qd);
   long qa[NB];
   load_q_operands<D>(s_qc, qa);
   float dqs[4][NB];
@@ -471,9 +742,9 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p) {
     const int v = p.causal ? L - p.n_qtok + r / G + 1 : L;
     vis[i] = min(r < R ? v : 0, c1);
   }
-  __syncthreads();
-  if (NSLOT == 2 && t_first + kStride < c1)
-    issue_tile<D, VF>(p, seq, kvh, t_first + kStride, ring_lds + S::BYTES, tl);
+  __syncthreads();   // every wave has its operands; wave 0's last slot is free
+  if (S::NSLOT == 2 && tq.n1 < c1) issue_tile<D, VF>(p, seq, kvh, tq.n1, ring_lds + S::BYTES, tl, cur);
+  tq.g = grab_tile(&s_next, c0);
 
   WaveState<D> st;
 #pragma unroll
@@ -483,173 +754,286 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p) {
     st.mrow[i] = -1e30f;
     st.lrow[i] = 0.0f;
   }
+  uint8_t* ring = s_lds + wave * S::NSLOT * S::BYTES;
+  float* pbuf = reinterpret_cast<float*>(s_lds + kWaves * S::NSLOT * S::BYTES + wave * S::PBYTES);
+  auto body = [&](auto slot_c, int t0) {
+    constexpr int SL = decltype(slot_c)::value;
+    process_tile<D, VF>(ring + SL * S::BYTES, pbuf, t0, c1, qa, dqs, vis, st);
+  };
+  run_ring<D, VF>(p, seq, kvh, c0, c1, &s_next, ring_lds, tl, cur, tq, body);
 
-  int slot = 0;
-  for (int t0 = t_first; t0 < c1; t0 += kStride) {
-    int pending;
-    if constexpr (NSLOT == 3) {
-      // issue the tile after next into the slot freed last step, then wait
-      // for this one (at most two younger tiles stay in flight)
-      const bool more = t0 + 2 * kStride < c1;
-      if (more) issue_tile<D, VF>(p, seq, kvh, t0 + 2 * kStride, ring_lds + ((slot + 2) % 3) * S::BYTES, tl);
-      pending = more ? 2 : (t0 + kStride < c1 ? 1 : 0);
-    } else {
-      pending = t0 + kStride < c1 ? 1 : 0;
-    }
-    wait_tiles<LPT>(pending);
-    process_tile<D, VF>(ring + slot * S::BYTES, pbuf, t0, c1, qa, dqs, vis, st);
-    if constexpr (NSLOT == 2) {
-      if (t0 + 2 * kStride < c1)
-        issue_tile<D, VF>(p, seq, kvh, t0 + 2 * kStride, ring_lds + slot * S::BYTES, tl);
-    }
-    slot = (slot + 1 == NSLOT) ? 0 : slot + 1;
-  }
-  v4f(&acc)[NT] = st.acc;
-  float(&mrow)[4] = st.mrow;
-  float(&lrow)[4] = st.lrow;
-
-  // ---- merge the four waves through LDS; one partial per work-group
+  // ---- this wave's rows to LDS for the merge
   float* s_buf = reinterpret_cast<float*>(s_lds);
   float* s_m = s_buf + kWaves * kRows * D;
   float* s_l = s_m + kWaves * kRows;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lrow[i] = sum_row16(lrow[i]);
+  for (int i = 0; i < 4; ++i) st.lrow[i] = sum_row16(st.lrow[i]);
   __syncthreads();   // every wave is done with its ring
 #pragma unroll
   for (int n = 0; n < NT; ++n)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_buf[(wave * kRows + 4 * grp + i) * D + 16 * n + col] = acc[n][i];
+    for (int i = 0; i < 4; ++i) s_buf[(wave * kRows + 4 * grp + i) * D + 16 * n + col] = st.acc[n][i];
   if (col == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s_m[wave * kRows + 4 * grp + i] = mrow[i];
-      s_l[wave * kRows + 4 * grp + i] = lrow[i];
+      s_m[wave * kRows + 4 * grp + i] = st.mrow[i];
+      s_l[wave * kRows + 4 * grp + i] = st.lrow[i];
     }
   }
   __syncthreads();
+  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq);
+}
 
-  // Partials go out with agent-scope stores (write-through, coherent across
-  // XCDs once complete), so publishing needs only a wait for the stores and
-  // the counter increment, not a write-back of the whole L2.
-  const size_t pbase = ((size_t)seq * p.n_kv_heads + kvh) * p.n_split;
-  for (int e = tid; e < R * D; e += 256) {
-    const int r = e / D;
-    float M = s_m[r];
+// ---------------------------------------------------------------------------
+// Column layout
+// ---------------------------------------------------------------------------
+
+// Per-lane state: acc[g][i] = sum over tokens of p * V for dim 16g + 4*(l/16)
+// + i of this lane's column; m is the row's running maximum (log2 domain),
+// c0 = -m on the block-0 lane of a live row (so the block sum yields score - m)
+// and -1e30 on the block-0 lane of a padding column; l sums this lane's
+// weights.
+template <int D>
+struct ColState {
+  v4f acc[D / 16];
+  float m;
+  float c0;
+  float l;
+};
+
+// Lanes of one row (its NB block columns) sit next to each other; the
+// butterfly adds their values.
+template <int NB>
+__device__ __forceinline__ float sum_blocks(float x) {
+  x += dpp_f<0xB1>(x);
+  if constexpr (NB == 4) x += dpp_f<0x4E>(x);
+  return x;
+}
+
+template <int D, int VF>
+__device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, int c1, bool full,
+                                                  bool first, int vis, bool valid,
+                                                  const long (&qb)[D / kBlock], float wq,
+                                                  ColState<D>& st) {
+  using S = Slot<D, VF>;
+  constexpr int NB = D / kBlock;
+  constexpr int NG = D / 16;
+  const int lane = __lane_id();
+  const int col = lane & 15, grp = lane >> 4;
+  const int b = col % NB;
+
+  // ---- int32 block dots.  Half h feeds row m of A with the K row of token
+  // 8*(m/4) + 4h + m%4, so output row 4*grp + i of half h is token
+  // 8*grp + 4h + i: this lane ends up with tokens 8*grp .. +8 in order.
+  v4i cq[2];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w * kRows + r]);
-    float o = 0.0f, l = 0.0f;
+  for (int h = 0; h < 2; ++h) {
+    cq[h] = (v4i){0, 0, 0, 0};
+    const int tau = 8 * (col >> 2) + 4 * h + (col & 3);
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float a = __builtin_amdgcn_exp2f(s_m[w * kRows + r] - M);
-      o = fmaf(a, s_buf[(w * kRows + r) * D + (e - r * D)], o);
-      l = fmaf(a, s_l[w * kRows + r], l);
+    for (int bb = 0; bb < NB; ++bb) {
+      const int q = 2 * bb + (grp >> 1);
+      const long ka = *reinterpret_cast<const long*>(
+          slot + S::K_OFF + (tau * S::CPR + (q ^ (tau % S::CPR))) * 16 + 8 * (grp & 1));
+      cq[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ka, qb[bb], cq[h], 0, 0, 0);
     }
-    __hip_atomic_store(&p.part_o[((pbase + split) * R) * D + e], o, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    if (e - r * D == 0) {
-      __hip_atomic_store(&p.part_ml[((pbase + split) * R + r) * 2], M, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.part_ml[((pbase + split) * R + r) * 2 + 1], l, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // ---- scores minus the running maximum, log2 domain, tokens t0 + 8*grp + j
+  const uint4 dkw = *reinterpret_cast<const uint4*>(slot + S::DK_OFF + b * 64 + 16 * grp);
+  const uint32_t dkv[4] = {dkw.x, dkw.y, dkw.z, dkw.w};
+  float s[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float w = (j & 1) ? mul_f32_f16<1>(wq, dkv[j >> 1]) : mul_f32_f16<0>(wq, dkv[j >> 1]);
+    s[j] = fmaf((float)cq[j >> 2][j & 3], w, st.c0);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) s[j] = sum_blocks<NB>(s[j]);
+  if (!full) {
+    const int lim = vis - t0 - 8 * grp;   // tokens j >= lim are not visible
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j >= lim) s[j] = -INFINITY;
+  }
+  float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+  if (!valid) mx = -INFINITY;
+  if (first || __any(mx > 0.0f)) {
+    // row maximum over the four lane groups (the block lanes agree already)
+    float rm = fmaxf(mx, shfl_xor_f(mx, 16));
+    rm = fmaxf(rm, shfl_xor_f(rm, 32));
+    float delta;
+    if (first) {
+      delta = rm == -INFINITY ? 0.0f : rm;   // nothing accumulated yet
+    } else {
+      delta = fmaxf(rm, 0.0f);
+      const float a = __builtin_amdgcn_exp2f(-delta);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) st.acc[g] *= a;
+      st.l *= a;
+    }
+    st.m += delta;
+    if (b == 0 && valid) st.c0 -= delta;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[j] -= delta;
+  }
+  float pj[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    pj[j] = __builtin_amdgcn_exp2f(s[j]);
+    st.l += pj[j];
+  }
+
+  // ---- B operand: p * d_v of this column's block as fp16 hi + lo
+  const uint4 dvw = *reinterpret_cast<const uint4*>(slot + S::DV_OFF + b * 64 + 16 * grp);
+  uint32_t dv[4] = {dvw.x, dvw.y, dvw.z, dvw.w};
+  if (!full) {
+    // tokens past the chunk end may hold anything (even non-finite scales)
+    const int lim = c1 - t0 - 8 * grp;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j >= lim) dv[j >> 1] &= (j & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+  }
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) split_f16_pair(pj[2 * k], pj[2 * k + 1], dv[k], hw[k], lw[k]);
+  const v8h bhi = __builtin_bit_cast(v8h, hw);
+  const v8h blo = __builtin_bit_cast(v8h, lw);
+
+  // ---- (P.V)^T: A = V codes of dims 16g + col, tokens 8*grp .. +8
+  if constexpr (VF == 0) {
+#pragma unroll
+    for (int bb = 0; bb < NB; ++bb) {
+      // byte = nibble(dim 32bb + col) | nibble(dim 32bb + 16 + col) << 4; the
+      // high nibble is used in place, as 16 * (n - 8) (exact), and the factor
+      // 16 is taken out of those accumulators at the end
+      const int R = 16 * bb + col;
+      const uint2 w = *reinterpret_cast<const uint2*>(
+          slot + S::V_OFF + (R * 2 + ((grp >> 1) ^ ((R >> 2) & 1))) * 16 + 8 * (grp & 1));
+      const v8h alo = bytes_to_f16x8(w.x & 0x0F0F0F0Fu, w.y & 0x0F0F0F0Fu, (_Float16)1032.0f);
+      const v8h ahi = bytes_to_f16x8(w.x & 0xF0F0F0F0u, w.y & 0xF0F0F0F0u, (_Float16)1152.0f);
+      st.acc[2 * bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bhi, st.acc[2 * bb], 0, 0, 0);
+      st.acc[2 * bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, blo, st.acc[2 * bb], 0, 0, 0);
+      st.acc[2 * bb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bhi, st.acc[2 * bb + 1], 0, 0, 0);
+      st.acc[2 * bb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, blo, st.acc[2 * bb + 1], 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int R = 16 * g + col;
+      const uint2 w = *reinterpret_cast<const uint2*>(
+          slot + S::V_OFF + (R * 2 + ((grp >> 1) ^ ((R >> 2) & 1))) * 16 + 8 * (grp & 1));
+      // int8 code c -> byte c ^ 0x80 = c + 128 -> fp16 (1024 + c + 128) - 1152
+      const v8h av = bytes_to_f16x8(w.x ^ 0x80808080u, w.y ^ 0x80808080u, (_Float16)1152.0f);
+      st.acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bhi, st.acc[g], 0, 0, 0);
+      st.acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, blo, st.acc[g], 0, 0, 0);
     }
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  if (tid == 0) {
-    const unsigned done = __hip_atomic_fetch_add(&p.counters[(size_t)seq * p.n_kv_heads + kvh], 1u,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = (done == (unsigned)(n_split_seq - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  // The last group of this (sequence, kv head): drop stale cached lines, then
-  // merge the partials of every split.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
 
-  const int nsp = n_split_seq;
-  float* sw = s_buf;                      // [nsp][R] split maxima, then weights
-  float* sl = s_buf + nsp * R;            // [nsp][R] split sums
-  float4* red = reinterpret_cast<float4*>(s_buf + 2 * kMaxSplits * kRows);
-  for (int i = tid; i < nsp * R; i += 256) {
-    const int sp = i / R, r = i - sp * R;
-    const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + ((pbase + sp) * R + r) * 2);
-    sw[i] = ml.x;
-    sl[i] = ml.y;
-  }
-  __syncthreads();
-  if (tid < R) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < nsp; ++sp) M = fmaxf(M, sw[sp * R + tid]);
-    float den = 0.0f;
-    for (int sp = 0; sp < nsp; ++sp)
-      den = fmaf(__builtin_amdgcn_exp2f(sw[sp * R + tid] - M), sl[sp * R + tid], den);
-    s_m[tid] = M;
-    s_l[tid] = 1.0f / den;
-  }
-  __syncthreads();
-  for (int i = tid; i < nsp * R; i += 256) {
-    const int r = i % R;
-    sw[i] = __builtin_amdgcn_exp2f(sw[i] - s_m[r]) * s_l[r];
-  }
-  __syncthreads();
+template <int D, int VF>
+__global__ __launch_bounds__(kThreads) void k_attn_cols(AttnParams p) {
+  using S = Slot<D, VF>;
+  constexpr int NB = D / kBlock;
+  constexpr int NG = D / 16;
+  constexpr int RING = kWaves * S::NSLOT * S::BYTES;
+  constexpr int MERGE = kWaves * kRows * D * 4 + 2 * kWaves * kRows * 4;
+  constexpr int LDS_BYTES = RING > MERGE ? RING : MERGE;
 
-  // Outputs as float4 columns; 256 / cols threads share a column, each summing
-  // every tpc-th split with eight loads in flight.
-  const int cols = R * D / 4;
-  const int tpc = cols >= 256 ? 1 : 256 / cols;
-  for (int c = tid; c < cols * tpc; c += 256) {
-    const int cc = c % cols, part = c / cols;
-    const int r = (4 * cc) / D;
-    const float* ob = p.part_o + (pbase * R) * D + 4 * cc;
-    float4 a = {0.0f, 0.0f, 0.0f, 0.0f};
-    int sp = part;
-    for (; sp + 7 * tpc < nsp; sp += 8 * tpc) {
-      float4 v[8];
+  __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
+  __shared__ int s_last;
+  __shared__ int s_next;   // next dynamically handed-out tile of the chunk
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, grp = lane >> 4;
+  const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
+  const int L = p.seq_len[seq];
+  const int n_split_seq = (L + p.chunk - 1) / p.chunk;
+  if (split >= n_split_seq) return;
+  const int c0 = split * p.chunk;
+  const int c1 = min(c0 + p.chunk, L);
+  const int R = p.rows, G = p.group;
+  const TileLane<D, VF> tl = tile_lane_offsets<D, VF>(lane);
+  TileCursor cur = {-1, 0};
+  TileQueue tq = {c0 + kTile * wave, c0 + kTile * (wave + kWaves), 0};
+  const uint32_t ring_lds = lds_addr(s_lds + wave * S::NSLOT * S::BYTES);
+  if (tid == 0) s_next = 2 * kWaves;
+
+  int8_t* s_qc;
+  float* s_qd;
+  prologue<D, VF>(p, s_lds, seq, kvh, wave, c1, tl, cur, tq, s_qc, s_qd);
+
+  // column (row r, block b); B operands hold row r's Q codes of block bb in
+  // the columns of block bb only
+  const int r = col / NB, b = col % NB;
+  const bool valid = r < R;
+  long qb[NB];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
-        v[u] = *reinterpret_cast<const float4*>(ob + (size_t)(sp + u * tpc) * R * D);
+  for (int bb = 0; bb < NB; ++bb)
+    qb[bb] = (valid && bb == b) ? *reinterpret_cast<const long*>(s_qc + r * D + kBlock * bb + 8 * grp) : 0;
+  const float wq = valid ? s_qd[r * NB + b] * p.scale_log2 : 0.0f;
+  const int vis = valid ? min(p.causal ? L - p.n_qtok + r / G + 1 : L, c1) : 0;
+  const int vis_min = min(p.causal ? L - p.n_qtok + 1 : L, c1);   // the first query token's
+  __syncthreads();   // every wave has its operands; wave 0's last slot is free
+  if (S::NSLOT == 2 && tq.n1 < c1) issue_tile<D, VF>(p, seq, kvh, tq.n1, ring_lds + S::BYTES, tl, cur);
+  tq.g = grab_tile(&s_next, c0);
+
+  ColState<D> st;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const float w = sw[(sp + u * tpc) * R + r];
-        a.x = fmaf(w, v[u].x, a.x);
-        a.y = fmaf(w, v[u].y, a.y);
-        a.z = fmaf(w, v[u].z, a.z);
-        a.w = fmaf(w, v[u].w, a.w);
+  for (int g = 0; g < NG; ++g) st.acc[g] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+  st.m = 0.0f;
+  st.c0 = (b == 0 && !valid) ? -1e30f : 0.0f;
+  st.l = 0.0f;
+
+  const uint8_t* ring = s_lds + wave * S::NSLOT * S::BYTES;
+  bool first = true;
+  auto body = [&](auto slot_c, int t0) {
+    constexpr int SL = decltype(slot_c)::value;
+    process_tile_cols<D, VF>(ring + SL * S::BYTES, t0, c1, t0 + kTile <= vis_min, first, vis, valid,
+                             qb, wq, st);
+    first = false;
+  };
+  run_ring<D, VF>(p, seq, kvh, c0, c1, &s_next, ring_lds, tl, cur, tq, body);
+
+  // ---- this wave's rows to LDS for the merge
+  float* s_buf = reinterpret_cast<float*>(s_lds);
+  float* s_m = s_buf + kWaves * kRows * D;
+  float* s_l = s_m + kWaves * kRows;
+  float l = st.l;
+  l += shfl_xor_f(l, 16);
+  l += shfl_xor_f(l, 32);
+  __syncthreads();   // every wave is done with its ring
+  if (valid) {
+    // q4_0 high-nibble dims (odd g) were accumulated 16 times too large
+    constexpr float kHi = VF == 0 ? 0.0625f : 1.0f;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      if ((g >> 1) == b) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s_buf[(wave * kRows + r) * D + 16 * g + 4 * grp + i] = (g & 1) ? st.acc[g][i] * kHi : st.acc[g][i];
       }
+    if (b == 0 && grp == 0) {
+      s_m[wave * kRows + r] = l > 0.0f ? st.m : -1e30f;
+      s_l[wave * kRows + r] = l;
     }
-    for (; sp < nsp; sp += tpc) {
-      const float4 v = *reinterpret_cast<const float4*>(ob + (size_t)sp * R * D);
-      const float w = sw[sp * R + r];
-      a.x = fmaf(w, v.x, a.x);
-      a.y = fmaf(w, v.y, a.y);
-      a.z = fmaf(w, v.z, a.z);
-      a.w = fmaf(w, v.w, a.w);
-    }
-    red[c] = a;
   }
   __syncthreads();
-  for (int cc = tid; cc < cols; cc += 256) {
-    float4 a = red[cc];
-    for (int part = 1; part < tpc; ++part) {
-      const float4 b = red[part * cols + cc];
-      a.x += b.x;
-      a.y += b.y;
-      a.z += b.z;
-      a.w += b.w;
-    }
-    const int r = (4 * cc) / D;
-    const int d = 4 * cc - r * D;
-    const int j = r / G;
-    const int h = kvh * G + r % G;
-    *reinterpret_cast<float4*>(p.out + (((size_t)seq * p.n_qtok + j) * p.n_q_heads + h) * D + d) = a;
-  }
-  if (tid == 0)
-    __hip_atomic_store(&p.counters[(size_t)seq * p.n_kv_heads + kvh], 0u, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq);
 }
 
 bool attn_supported(int head_dim, int v_format) {
   return (head_dim == 64 || head_dim == 128) && (v_format == 0 || v_format == 1);
+}
+
+template <int D, int VF>
+static void launch_attn_kernel(const AttnParams& p, dim3 grid, hipStream_t stream) {
+  if (p.rows * (D / kBlock) <= 16)
+    hipLaunchKernelGGL((k_attn_cols<D, VF>), grid, dim3(kThreads), 0, stream, p);
+  else
+    hipLaunchKernelGGL((k_attn_rows<D, VF>), grid, dim3(kThreads), 0, stream, p);
 }
 
 int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
@@ -684,14 +1068,14 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
   const dim3 grid(plan.n_split, c.n_kv_heads, n_seq);
   if (c.head_dim == 128) {
     if (c.v_format == 0)
-      hipLaunchKernelGGL((k_attn_split<128, 0>), grid, dim3(256), 0, stream, p);
+      launch_attn_kernel<128, 0>(p, grid, stream);
     else
-      hipLaunchKernelGGL((k_attn_split<128, 1>), grid, dim3(256), 0, stream, p);
+      launch_attn_kernel<128, 1>(p, grid, stream);
   } else {
     if (c.v_format == 0)
-      hipLaunchKernelGGL((k_attn_split<64, 0>), grid, dim3(256), 0, stream, p);
+      launch_attn_kernel<64, 0>(p, grid, stream);
     else
-      hipLaunchKernelGGL((k_attn_split<64, 1>), grid, dim3(256), 0, stream, p);
+      launch_attn_kernel<64, 1>(p, grid, stream);
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }

@@ -26,7 +26,7 @@ struct WorkspaceLayout {
   size_t total;
 };
 
-constexpr int kChunkAlign = 128;   // 4 waves x 32-token tiles
+constexpr int kChunkAlign = 256;   // one 32-token tile for each of the 8 waves of a work-group
 constexpr int kMaxSplits = 64;     // splits per (sequence, kv head) the merge stages in LDS
 
 SplitPlan plan_splits(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads, int max_seq_len);

@@ -58,14 +58,15 @@ enum kvq_v_format {
  * laid out [n_segs][n_kv_heads][seg_tokens][...]:
  *   k_qs  uint32 [..][head_dim/4]   int8 K codes of one token per row,
  *                                   byte k of word w = element 4w+k
- *   k_d   uint16 [..][head_dim/32]  fp16 bit patterns, one per 32-block
+ *   k_d   uint16 [..][head_dim/32]  fp16 bit patterns, one per 32-block (tiled, below)
  *   v_qs  uint8  [..][vrow]         V payload, vrow = head_dim/2 (q4_0) or head_dim (q8_0)
- *   v_d   uint16 [..][head_dim/32]  fp16 bit patterns
- * K is token-major.  V is token-interleaved in tiles of 32 tokens (rows 32i ..
- * 32i+31 of a segment): inside a tile, byte k of token t's q4_0/q8_0 row is
- * stored at byte k*32 + t and scale b of token t at scale slot b*32 + t, so the
- * reduction axis of P.V is contiguous ("BitLLM", page 3, on matching the layout
- * to the reduction axis).  A q4_0 row holds, per 32-block, bytes
+ *   v_d   uint16 [..][head_dim/32]  fp16 bit patterns (tiled, below)
+ * K codes are token-major.  The scale planes and the V payload are
+ * token-interleaved in tiles of 32 tokens (rows 32i .. 32i+31 of a segment):
+ * inside a tile, scale b of token t sits at scale slot b*32 + t (K and V alike)
+ * and byte k of token t's q4_0/q8_0 row at byte k*32 + t, so the token axis,
+ * the reduction axis of P.V, is contiguous ("BitLLM", page 3, on matching the
+ * layout to the reduction axis).  A q4_0 row holds, per 32-block, bytes
  * j = 0..15 = nibble(element j) | nibble(element j+16) << 4.
  * Token t of sequence i lives in segment seg_table[i*max_segs + t/seg_tokens]
  * (or segment i*max_segs + t/seg_tokens when no table is given), at row

@@ -62,10 +62,9 @@ def gpu_rows(cache, ci: CacheInputs, i: int, tokens: np.ndarray):
     tile = torch.from_numpy((tokens - segj * seg_tokens).astype(np.int64) // 32).cuda()
     slot = torch.from_numpy((tokens - segj * seg_tokens).astype(np.int64) % 32).cuda()
     out = []
-    for plane in (cache.k_qs, cache.k_d):          # token-major rows
-        x = plane[segt, :, row]                    # [n][Hkv][...]
-        out.append(x.permute(1, 0, 2).contiguous().cpu().numpy())
-    for plane in (cache.v_qs, cache.v_d):          # 32-token tiles, [row byte][token]
+    x = cache.k_qs[segt, :, row]                   # K codes: token-major rows, [n][Hkv][...]
+    out.append(x.permute(1, 0, 2).contiguous().cpu().numpy())
+    for plane in (cache.k_d, cache.v_qs, cache.v_d):   # 32-token tiles, [row byte][token]
         s_, h_, _, w_ = plane.shape
         t5 = plane.view(s_, h_, ntile, w_, 32)
         x = t5[segt, :, tile, :, slot]             # [n][Hkv][w]
