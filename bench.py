@@ -15,6 +15,9 @@ the oracle timed on the host.
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
+import hashlib
 import json
 import os
 import sys
@@ -26,6 +29,94 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+CSRC = os.path.join(ROOT, "decode_attention_packed_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_long128k.txt")
+CALIB_BYTES = 256 << 20   # known sizes read / written by the calibration kernels
+ATTN_KERNEL = "k_attn_cols<128, 0>"
+
+
+def kernel_source_hash() -> str:
+    """sha256 over the kernel sources: a traffic summary is only valid for
+    the sources it was measured on."""
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def read_traffic() -> int | None:
+    """Calibrated HBM bytes per attention launch from the committed counter
+    summary, or None when it is missing or stale."""
+    try:
+        kv = {}
+        with open(TRAFFIC_FILE) as fh:
+            for line in fh:
+                if "=" in line and not line.startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        return int(float(kv["attn_traffic_bytes"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def _counter_rows(d: str, counter: str) -> dict:
+    """Per-kernel lists of one counter's per-dispatch values from a
+    rocprofv3 --pmc output directory."""
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") == counter:
+                    out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, fetch_cmd: str, write_cmd: str) -> str:
+    """Turn the FETCH_SIZE and WRITE_SIZE runs into the traffic summary:
+    each counter is scaled by what it reads for a kernel of known size (the
+    library's stream-read kernel for fetches, a device copy for writes)."""
+    fetch = _counter_rows(fetch_dir, "FETCH_SIZE")
+    write = _counter_rows(write_dir, "WRITE_SIZE")
+
+    def med(d, key):
+        vals = [v for k, vs in d.items() if key in k for v in vs]
+        if not vals:
+            raise SystemExit(f"no dispatches of {key} in the counter output")
+        return float(np.median(vals)), len(vals)
+
+    rd_kib, n_rd = med(fetch, "k_debug_stream_read")
+    cp_kib, n_cp = med(write, "copyBuffer")
+    at_f, n_af = med(fetch, ATTN_KERNEL)
+    at_w, n_aw = med(write, ATTN_KERNEL)
+    ffac = CALIB_BYTES / (rd_kib * 1024)
+    wfac = CALIB_BYTES / (cp_kib * 1024)
+    fb = at_f * 1024 * ffac
+    wb = at_w * 1024 * wfac
+    from decode_attention_packed_amd import workloads as W
+    alg = algorithmic_bytes(W.WORKLOADS["long128k"].caches[0], 131072, 1)["attn"]
+    lines = [
+        "# HBM traffic of one attention launch on the long128k workload, from rocprofv3",
+        "# counters (KiB per dispatch, medians), each scaled by the same counter read",
+        f"# for a kernel of known size ({CALIB_BYTES} bytes read / written).",
+        f"# fetch run: {fetch_cmd}",
+        f"# write run: {write_cmd}",
+        f"kernel_source_sha256 = {kernel_source_hash()}",
+        f"calib_read_fetch_kib = {rd_kib:.1f}   # k_debug_stream_read, {n_rd} dispatches",
+        f"calib_copy_write_kib = {cp_kib:.1f}   # device copy, {n_cp} dispatches",
+        f"fetch_factor = {ffac:.4f}",
+        f"write_factor = {wfac:.4f}",
+        f"attn_fetch_kib = {at_f:.1f}   # {ATTN_KERNEL}, {n_af} dispatches",
+        f"attn_write_kib = {at_w:.1f}   # {n_aw} dispatches",
+        f"attn_fetch_bytes = {fb:.0f}",
+        f"attn_write_bytes = {wb:.0f}",
+        f"attn_traffic_bytes = {fb + wb:.0f}",
+        f"algorithmic_bytes = {alg}",
+        f"traffic_over_algorithmic = {(fb + wb) / alg:.4f}",
+    ]
+    return "\n".join(lines) + "\n"
 
 
 def algorithmic_bytes(spec, n_tokens: int, append_rows: int) -> dict:
@@ -79,7 +170,18 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-sample-heads", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="also run the known-size read and copy kernels (for counter runs)")
+    ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "FETCH_CMD", "WRITE_CMD"),
+                    help="write the traffic summary from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_pmc:
+        text = summarize_pmc(*args.summarize_pmc)
+        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+        with open(TRAFFIC_FILE, "w") as fh:
+            fh.write(text)
+        print(text, end="")
+        return 0
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the path is not "
                                    "sharded across GPUs", "n_gpus": args.gpus}))
@@ -148,6 +250,45 @@ def main() -> int:
     torch.cuda.synchronize()
     attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
 
+    # warm cache: one replica, so most of it stays in the 256 MB Infinity Cache
+    for i in range(args.warmup):
+        step(0)
+    w0 = torch.cuda.Event(enable_timing=True)
+    w1 = torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for i in range(args.steps):
+        step(0)
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / args.steps
+
+    # HBM read ceiling: the library's plain 16-byte streaming read over 1 GiB
+    # (skipped in counter runs, whose only reads of that kernel are the
+    # known-size calibration ones)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    read_gbs = None
+    if not args.calibrate:
+        buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            K.kvq_debug_stream_read(buf, sink, stream=stream)
+        r0 = torch.cuda.Event(enable_timing=True)
+        r1 = torch.cuda.Event(enable_timing=True)
+        r0.record(stream)
+        for _ in range(10):
+            K.kvq_debug_stream_read(buf, sink, stream=stream)
+        r1.record(stream)
+        torch.cuda.synchronize()
+        read_gbs = round(buf.numel() / (r0.elapsed_time(r1) / 10 * 1e-3) / 1e9, 1)
+        del buf
+    else:
+        a = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            K.kvq_debug_stream_read(a, sink, stream=stream)
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
     nbytes = algorithmic_bytes(spec, L, 1)
     gbs = nbytes["step"] / (ms_step * 1e-3) / 1e9
     attn_mean_s = float(attn_ms.mean()) * 1e-3
@@ -175,7 +316,12 @@ def main() -> int:
                     "p50": round(float(np.percentile(attn_ms, 50)) * 1e3, 2),
                     "p90": round(float(np.percentile(attn_ms, 90)) * 1e3, 2)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": read_traffic()},
+        "read_ceiling_gbs": read_gbs,
+        "warm_single_replica": {"us_per_step": round(warm_ms * 1e3, 2),
+                                "gbs": round(nbytes["step"] / (warm_ms * 1e-3) / 1e9, 1),
+                                "note": "one cache replica, mostly resident in the Infinity Cache"},
     }
     print(f"[bench] timed: {ms_step * 1e3:.2f} us/step, attention {attn_ms.mean() * 1e3:.2f} us",
           file=sys.stderr, flush=True)

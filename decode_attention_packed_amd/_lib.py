@@ -27,7 +27,7 @@ KVQ_MAX_QTOK = 16
 
 EXPORTS = ("kvq_abi_version", "kvq_status_string", "kvq_cache_bytes", "kv_append_quant",
            "attn_decode_packed_workspace_size", "attn_decode_packed", "kvq_debug_quant_q",
-           "kvq_debug_qk_isum")
+           "kvq_debug_qk_isum", "kvq_debug_stream_read")
 
 
 class KvqCacheStruct(ctypes.Structure):
@@ -69,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_packed.argtypes = [P, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_int,
                                          c_void_p, c_int, c_float, c_int, c_void_p, c_size_t,
                                          c_void_p]
+        L.kvq_debug_stream_read.restype = c_int
+        L.kvq_debug_stream_read.argtypes = [c_void_p, ctypes.c_size_t, c_void_p, c_void_p]
         L.kvq_debug_quant_q.restype = c_int
         L.kvq_debug_quant_q.argtypes = [c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p]
         L.kvq_debug_qk_isum.restype = c_int
@@ -211,6 +213,16 @@ def attn_decode_packed(cache: PackedKVCache, q, out, seq_len, max_seq_len: int, 
                                     int(max_seq_len), float(sm_scale), int(bool(causal)),
                                     _ptr(workspace), ws_bytes, _stream(stream)),
            "attn_decode_packed")
+
+
+def kvq_debug_stream_read(buf, sink, stream=None) -> None:
+    """Stream-read every byte of the device tensor `buf` (contiguous, size a
+    multiple of 16); `sink` is a device int32/uint32 tensor of >= 1 element."""
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_cuda or not buf.is_contiguous() or not sink.is_cuda:
+        raise ValueError("buf and sink must be contiguous device tensors")
+    _check(lib().kvq_debug_stream_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)),
+           "kvq_debug_stream_read")
 
 
 def kvq_debug_quant_q(q, codes, scales, stream=None) -> None:

@@ -181,6 +181,13 @@ int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n
   return r ? KVQ_ERR_HIP : KVQ_OK;
 }
 
+int kvq_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (!buf || !sink || !aligned16(buf) || bytes % 16 || bytes == 0) return KVQ_ERR_INVALID;
+  return kvq::launch_debug_stream_read(buf, bytes, sink, static_cast<hipStream_t>(stream))
+             ? KVQ_ERR_HIP
+             : KVQ_OK;
+}
+
 int kvq_debug_quant_q(const float* q, int n_rows, int head_dim, int8_t* codes, float* scales,
                       void* stream) {
   if (!q || !codes || !scales || !aligned16(q) || !aligned16(codes) || !aligned16(scales))

@@ -61,6 +61,39 @@ __global__ __launch_bounds__(64) void k_debug_isum(const uint32_t* k_qs, const f
   }
 }
 
+// Plain streaming read of a buffer with 16-byte loads, eight per thread in
+// flight: the HBM read ceiling the attention kernels are measured against.
+// Each work-group reads whole 32 KB segments in turn; the xor of the data is
+// stored only in the unlikely case that it equals a sentinel, so the loads
+// cannot be dropped.
+__global__ __launch_bounds__(256) void k_debug_stream_read(const uint4* src, size_t n16,
+                                                           uint32_t* sink) {
+  constexpr int U = 8;
+  const size_t seg = (size_t)256 * U;
+  uint32_t acc = 0;
+  for (size_t base = (size_t)blockIdx.x * seg; base < n16; base += (size_t)gridDim.x * seg) {
+    if (base + seg <= n16) {
+      uint4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) v[u] = src[base + u * 256 + threadIdx.x];
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    } else {
+      for (size_t i = base + threadIdx.x; i < n16; i += 256) {
+        const uint4 x = src[i];
+        acc ^= x.x ^ x.y ^ x.z ^ x.w;
+      }
+    }
+  }
+  if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
+int launch_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  hipLaunchKernelGGL(k_debug_stream_read, dim3(2048), dim3(256), 0, stream,
+                     static_cast<const uint4*>(buf), bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
 int launch_debug_quant_q(const float* q, int n_rows, int head_dim, int8_t* codes, float* scales,
                          hipStream_t stream) {
   hipLaunchKernelGGL(k_debug_quant_q, dim3(n_rows), dim3(64), 0, stream, q, head_dim, codes, scales);

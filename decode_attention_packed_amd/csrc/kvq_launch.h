@@ -45,6 +45,7 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
                 hipStream_t stream);
 
+int launch_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 int launch_debug_quant_q(const float* q, int n_rows, int head_dim, int8_t* codes, float* scales,
                          hipStream_t stream);
 int launch_debug_isum(const kvq_cache& c, const float* q, int n_seq, int n_qtok, int n_q_heads,

@@ -165,6 +165,14 @@ int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n
  */
 int kvq_debug_quant_q(const float* q, int n_rows, int head_dim, int8_t* codes, float* scales,
                       void* stream);
+/*
+ * kvq_debug_stream_read: measurement hook, not part of the method.  Reads
+ * `bytes` (a nonzero multiple of 16) of device memory at `buf` (16-byte
+ * aligned) with plain 16-byte loads and discards them; `sink` (device, one
+ * uint32) is written only by chance.  Timed, it gives the HBM read rate a
+ * streaming kernel reaches on the device, the ceiling for the kernels above.
+ */
+int kvq_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 int kvq_debug_qk_isum(const kvq_cache* cache, const float* q, int n_seq, int n_qtok,
                       int n_q_heads, const int32_t* seg_table, int max_segs,
                       const int32_t* seq_len, int max_seq_len, int32_t* isum, void* stream);
