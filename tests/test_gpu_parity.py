@@ -212,6 +212,25 @@ def test_attention_multi_query(Tq, G, causal, L, fmt):
     H.assert_close(got, H.oracle_attention(ci), f"Tq{Tq} G{G} causal{causal} L{L}")
 
 
+@pytest.mark.parametrize("D,Tq,G,L,fmt", [(128, 2, 2, 517, 0), (128, 4, 1, 1000, 1),
+                                           (128, 3, 1, 64, 0), (64, 4, 2, 4200, 0),
+                                           (64, 2, 4, 300, 1), (128, 2, 1, 2, 0)])
+def test_attention_multi_query_column_layout(D, Tq, G, L, fmt):
+    """Causal multi-token groups small enough for the column layout
+    (rows x blocks <= 16), including a context equal to the query count."""
+    rng = np.random.default_rng(D + Tq * 100 + G * 10 + L)
+    Hkv = 2
+    spec = W.CacheSpec("mqc", 1, Tq, G * Hkv, Hkv, D, L, fmt, causal=True)
+    cap = -(-L // 64) * 64
+    ci = W.CacheInputs(spec, rng.standard_normal((1, Tq, G * Hkv, D)).astype(np.float32),
+                       (rng.standard_normal((1, L, Hkv, D)) * 1.5).astype(np.float32),
+                       rng.standard_normal((1, L, Hkv, D)).astype(np.float32),
+                       np.array([L], np.int32), None, 1, cap)
+    cache, table, max_segs = H.build_cache(ci)
+    got = H.run_attention(cache, ci, table, max_segs)
+    H.assert_close(got, H.oracle_attention(ci), f"cols D{D} Tq{Tq} G{G} L{L}")
+
+
 def test_attention_verify_small():
     # the speculative-verify recipe (main 32/8 and draft 16/4, 4 causal query
     # tokens) at a short context, every output checked
