@@ -81,7 +81,38 @@ struct AttnParams {
   int n_split;
   int causal;
   float scale_log2;       // sm_scale * log2(e)
+  int xcd_local;          // splits of a (sequence, kv head) share an XCD (see block_coords)
 };
+
+// Work-groups go to the 8 XCDs round-robin by linear index.  When the number
+// of (sequence, kv head) groups is a multiple of 8, linear index b runs group
+// (b % 8) + 8 * ((b / 8) / n_split), split (b / 8) % n_split, so all splits of
+// a group land on one XCD and share its L2; otherwise groups are consecutive.
+constexpr int kXcds = 8;
+struct BlockCoords {
+  int seq, kvh, split;
+  bool off_xcd;   // this work-group does not sit on the XCD its group expects
+};
+__device__ __forceinline__ BlockCoords block_coords(const AttnParams& p) {
+  const int b = blockIdx.x;
+  int g, split;
+  if (p.xcd_local) {
+    const int k = b / kXcds;
+    g = b % kXcds + kXcds * (k / p.n_split);
+    split = k % p.n_split;
+  } else {
+    g = b / p.n_split;
+    split = b % p.n_split;
+  }
+  unsigned xcc;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+  BlockCoords c;
+  c.seq = g / p.n_kv_heads;
+  c.kvh = g - c.seq * p.n_kv_heads;
+  c.split = split;
+  c.off_xcd = !p.xcd_local || (int)(xcc & 0xF) != b % kXcds;
+  return c;
+}
 
 // Geometry of one LDS ring slot for head_dim D and V format VF.
 template <int D, int VF>
@@ -386,7 +417,7 @@ __device__ __forceinline__ void split_f16_pair(float p0, float p1, uint32_t dpai
 // sequence with a single split writes its rows directly.
 template <int D, int LDS_BYTES>
 __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, int* s_last, int seq,
-                                             int kvh, int split, int n_split_seq) {
+                                             int kvh, int split, int n_split_seq, bool off_xcd) {
   constexpr int kBatch = 16;                              // partial loads in flight per thread
   static_assert(kMaxSplits * kRows * 4 + 16 * kThreads <= LDS_BYTES,
                 "split merge does not fit the LDS buffer");
@@ -433,16 +464,26 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, 
   if (single) return;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  // The counter's low 16 bits count finished splits; each work-group that is
+  // not on its group's XCD also adds 1 << 16.
   if (tid == 0) {
-    const unsigned done = __hip_atomic_fetch_add(&p.counters[(size_t)seq * p.n_kv_heads + kvh], 1u,
+    const unsigned inc = 1u + (off_xcd ? (1u << 16) : 0u);
+    const unsigned done = __hip_atomic_fetch_add(&p.counters[(size_t)seq * p.n_kv_heads + kvh], inc,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_last = (done == (unsigned)(n_split_seq - 1));
+    const bool last = (done & 0xFFFFu) == (unsigned)(n_split_seq - 1);
+    *s_last = last ? (((done + inc) >> 16) == 0 ? 2 : 1) : 0;
   }
   __syncthreads();
   if (!*s_last) return;
-  // The last group of this (sequence, kv head): drop stale cached lines, then
-  // merge the partials of every split.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // The last group of this (sequence, kv head) merges the partials of every
+  // split.  When every split ran on this XCD, their stores went through this
+  // L2 and only the CU's own cache needs dropping; otherwise stale lines of
+  // the whole L2 are dropped first.
+  if (*s_last == 2) {
+    asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
   static_assert(kMaxSplits <= 64, "one lane per split");
   const int nsp = n_split_seq;
   float* sw = s_buf;                                    // [nsp][R] split weights
@@ -714,7 +755,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_rows(AttnParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
+  const BlockCoords bc = block_coords(p);
+  const int split = bc.split, kvh = bc.kvh, seq = bc.seq;
   const int L = p.seq_len[seq];
   const int n_split_seq = (L + p.chunk - 1) / p.chunk;
   if (split >= n_split_seq) return;
@@ -781,7 +823,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_rows(AttnParams p) {
     }
   }
   __syncthreads();
-  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq);
+  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq, bc.off_xcd);
 }
 
 // ---------------------------------------------------------------------------
@@ -948,7 +990,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_cols(AttnParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const int split = blockIdx.x, kvh = blockIdx.y, seq = blockIdx.z;
+  const BlockCoords bc = block_coords(p);
+  const int split = bc.split, kvh = bc.kvh, seq = bc.seq;
   const int L = p.seq_len[seq];
   const int n_split_seq = (L + p.chunk - 1) / p.chunk;
   if (split >= n_split_seq) return;
@@ -1021,7 +1064,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_cols(AttnParams p) {
     }
   }
   __syncthreads();
-  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq);
+  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq, bc.off_xcd);
 }
 
 bool attn_supported(int head_dim, int v_format) {
@@ -1065,7 +1108,9 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
   p.n_split = plan.n_split;
   p.causal = causal;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
-  const dim3 grid(plan.n_split, c.n_kv_heads, n_seq);
+  const long long n_groups = (long long)n_seq * c.n_kv_heads;
+  p.xcd_local = n_groups % kXcds == 0;
+  const dim3 grid((unsigned)(n_groups * plan.n_split));
   if (c.head_dim == 128) {
     if (c.v_format == 0)
       launch_attn_kernel<128, 0>(p, grid, stream);
