@@ -75,22 +75,33 @@ def _counter_rows(d: str, counter: str) -> dict:
 
 
 def summarize_pmc(fetch_dir: str, write_dir: str, fetch_cmd: str, write_cmd: str) -> str:
-    """Turn the FETCH_SIZE and WRITE_SIZE runs into the traffic summary:
-    each counter is scaled by what it reads for a kernel of known size (the
-    library's stream-read kernel for fetches, a device copy for writes)."""
+    """Turn the FETCH_SIZE and WRITE_SIZE runs (of `bench.py --calibrate`)
+    into the traffic summary: each counter is scaled by what it reads for a
+    kernel of known size (the library's stream-read kernel over CALIB_BYTES
+    for fetches, a device copy of CALIB_BYTES for writes)."""
     fetch = _counter_rows(fetch_dir, "FETCH_SIZE")
     write = _counter_rows(write_dir, "WRITE_SIZE")
 
-    def med(d, key):
-        vals = [v for k, vs in d.items() if key in k for v in vs]
+    def pick(d, key):
+        return [v for k, vs in d.items() if key in k for v in vs]
+
+    def med(vals, what):
         if not vals:
-            raise SystemExit(f"no dispatches of {key} in the counter output")
+            raise SystemExit(f"no dispatches of {what} in the counter output")
         return float(np.median(vals)), len(vals)
 
-    rd_kib, n_rd = med(fetch, "k_debug_stream_read")
-    cp_kib, n_cp = med(write, "copyBuffer")
-    at_f, n_af = med(fetch, ATTN_KERNEL)
-    at_w, n_aw = med(write, ATTN_KERNEL)
+    # in a --calibrate run every stream read covers CALIB_BYTES; the same
+    # counter must then agree across them
+    rd = pick(fetch, "k_debug_stream_read")
+    if rd and max(rd) > 1.05 * min(rd):
+        raise SystemExit("stream-read dispatches of different sizes: use a --calibrate run")
+    rd_kib, n_rd = med(rd, "k_debug_stream_read")
+    # the calibration copies are the large ones; the small copies are input uploads
+    cp = pick(write, "copyBuffer")
+    cp = [v for v in cp if v >= 0.5 * max(cp)] if cp else cp
+    cp_kib, n_cp = med(cp, "the calibration copy")
+    at_f, n_af = med(pick(fetch, ATTN_KERNEL), ATTN_KERNEL)
+    at_w, n_aw = med(pick(write, ATTN_KERNEL), ATTN_KERNEL)
     ffac = CALIB_BYTES / (rd_kib * 1024)
     wfac = CALIB_BYTES / (cp_kib * 1024)
     fb = at_f * 1024 * ffac
@@ -119,6 +130,38 @@ def summarize_pmc(fetch_dir: str, write_dir: str, fetch_cmd: str, write_cmd: str
     return "\n".join(lines) + "\n"
 
 
+def summarize_trace(trace_dir: str, cmd: str, steps: int, warmup: int) -> str:
+    """Per-kernel statistics of a `rocprofv3 --kernel-trace --stats` run of
+    this benchmark, with the attention kernel's durations split by bench
+    phase (cold rotating replicas, per-step events, warm single replica)."""
+    stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    trace = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
+    if not stats or not trace:
+        raise SystemExit(f"no kernel trace under {trace_dir}")
+    lines = ["# Kernel durations of the long128k decode step (bench.py) from rocprofv3.",
+             f"# command: {cmd}",
+             "# kernel | calls | average us | min us | max us"]
+    with open(stats[0]) as fh:
+        for row in csv.DictReader(fh):
+            lines.append(f"{row['Name'][:90]} | {row['Calls']} | {float(row['AverageNs']) / 1e3:.2f} | "
+                         f"{float(row['MinNs']) / 1e3:.2f} | {float(row['MaxNs']) / 1e3:.2f}")
+    with open(trace[0]) as fh:
+        rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
+    att = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+           for r in rows if ATTN_KERNEL in r["Kernel_Name"]]
+    # bench order: warmup, timed steps, per-step events, warm warmup, warm steps
+    phases = [("cold warmup", warmup), ("cold timed steps", steps), ("cold per-step events", steps),
+              ("warm warmup", warmup), ("warm single replica", steps)]
+    lines.append(f"# {ATTN_KERNEL} by bench phase: phase | dispatches | average us | median us")
+    i = 0
+    for name, n in phases:
+        seg = np.array(att[i:i + n])
+        i += n
+        if seg.size:
+            lines.append(f"{name} | {seg.size} | {seg.mean():.2f} | {np.median(seg):.2f}")
+    return "\n".join(lines) + "\n"
+
+
 def algorithmic_bytes(spec, n_tokens: int, append_rows: int) -> dict:
     """K payload + K scales + V payload + V scales of every attended
     (token, kv head), plus the packed bytes written by the append."""
@@ -131,35 +174,35 @@ def algorithmic_bytes(spec, n_tokens: int, append_rows: int) -> dict:
     return {"attn": attn, "append": app, "step": attn + app, "per_token_head": kb + vb}
 
 
-def cpu_baseline(ci, kv_heads_sample: int) -> dict:
-    """The oracle on the host: the same step (quantize the new token, then
-    attention from the packed cache) for `kv_heads_sample` of the kv heads,
-    scaled to a whole step."""
+def cpu_baseline(ci, target_s: float = 12.0) -> dict:
+    """The oracle on the host: the same step (quantize the new token into
+    the packed cache, then attention over all tokens from the packed cache),
+    repeated for about `target_s` seconds; reported in the metric's unit."""
     from threadpoolctl import threadpool_limits
 
     from oracle import kvq_oracle as O
     spec = ci.spec
-    G = spec.n_q_heads // spec.n_kv_heads
     L = spec.ctx
-    heads = list(range(kv_heads_sample))
     with threadpool_limits(limits=1):
         # the packed cache is an input of the step, built outside the timing
-        kw, kd = O.encode_k(ci.k[0][:, heads].transpose(1, 0, 2))
-        vp, vd = O.encode_v(ci.v[0][:, heads].transpose(1, 0, 2), spec.v_format)
-        t0 = time.perf_counter()
-        nk, nkd = O.encode_k(ci.extra["append_k"][0, 0, heads])
-        nv, nvd = O.encode_v(ci.extra["append_v"][0, 0, heads], spec.v_format)
-        kw[:, L - 1], kd[:, L - 1], vp[:, L - 1], vd[:, L - 1] = nk, nkd, nv, nvd
-        q = ci.q[:, :, :kv_heads_sample * G]
-        O.decode_attention(q, kw[None], kd[None], vp[None], vd[None], spec.v_format, ci.seq_len,
-                           spec.sm_scale, False)
-        dt = time.perf_counter() - t0
-    scale = spec.n_kv_heads / kv_heads_sample
-    us = dt * scale * 1e6
-    return {"value": us, "unit": "us/step", "cores": 1, "kind": "oracle",
-            "sample": f"{kv_heads_sample} of {spec.n_kv_heads} kv heads of one step "
-                      f"({dt:.1f} s on the host, numpy float64, BLAS limited to 1 thread), "
-                      f"scaled x{scale:g}"}
+        kw, kd = O.encode_k(ci.k[0].transpose(1, 0, 2))
+        vp, vd = O.encode_v(ci.v[0].transpose(1, 0, 2), spec.v_format)
+        reps, t_total = 0, 0.0
+        while t_total < target_s:
+            t0 = time.perf_counter()
+            nk, nkd = O.encode_k(ci.extra["append_k"][0, 0])
+            nv, nvd = O.encode_v(ci.extra["append_v"][0, 0], spec.v_format)
+            kw[:, L - 1], kd[:, L - 1], vp[:, L - 1], vd[:, L - 1] = nk, nkd, nv, nvd
+            O.decode_attention(ci.q, kw[None], kd[None], vp[None], vd[None], spec.v_format,
+                               ci.seq_len, spec.sm_scale, False)
+            t_total += time.perf_counter() - t0
+            reps += 1
+    s_step = t_total / reps
+    step_bytes = algorithmic_bytes(spec, L, 1)["step"]
+    return {"value": round(step_bytes / s_step / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "us_per_step": round(s_step * 1e6, 1),
+            "sample": f"{reps} whole long128k steps (append 1 token + attention over 131072 tokens, "
+                      f"all 8 kv heads) in {t_total:.1f} s, numpy float64, BLAS limited to 1 thread"}
 
 
 def main() -> int:
@@ -168,13 +211,21 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--replicas", type=int, default=3)
-    ap.add_argument("--cpu-sample-heads", type=int, default=8)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run the known-size read and copy kernels (for counter runs)")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "CMD"),
+                    help="write the kernel-trace summary of a rocprofv3 run of this benchmark and exit")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "FETCH_CMD", "WRITE_CMD"),
                     help="write the traffic summary from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        text = summarize_trace(*args.summarize_trace, args.steps, args.warmup)
+        with open(os.path.join(ROOT, "profiles", "attn_kernel_trace_long128k.txt"), "w") as fh:
+            fh.write(text)
+        print(text, end="")
+        return 0
     if args.summarize_pmc:
         text = summarize_pmc(*args.summarize_pmc)
         os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
@@ -326,7 +377,7 @@ def main() -> int:
     print(f"[bench] timed: {ms_step * 1e3:.2f} us/step, attention {attn_ms.mean() * 1e3:.2f} us",
           file=sys.stderr, flush=True)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(ci, args.cpu_sample_heads)
+        result["cpu_baseline"] = cpu_baseline(ci, args.cpu_seconds)
     print(json.dumps(result), flush=True)
     return 0
 

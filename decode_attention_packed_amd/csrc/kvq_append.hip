@@ -35,16 +35,18 @@ struct AppendParams {
   int v_format;
 };
 
-// max over the 32 lanes of a half-wave
+// max / min over the 32 lanes of a half-wave: DPP inside each 16-lane row,
+// then one exchange between the two rows
 __device__ __forceinline__ float max32(float x) {
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) x = fmaxf(x, shfl_xor_f(x, m));
-  return x;
+  x = max_row16(x);
+  return fmaxf(x, shfl_xor_f(x, 16));
 }
 __device__ __forceinline__ int min32(int x) {
-#pragma unroll
-  for (int m = 1; m < 32; m <<= 1) x = min(x, __shfl_xor(x, m));
-  return x;
+  x = min(x, dpp_i<0xB1>(x));
+  x = min(x, dpp_i<0x4E>(x));
+  x = min(x, dpp_i<0x141>(x));
+  x = min(x, dpp_i<0x140>(x));
+  return min(x, __shfl_xor(x, 16));
 }
 
 __global__ __launch_bounds__(256) void k_append_quant(AppendParams p) {
@@ -53,8 +55,15 @@ __global__ __launch_bounds__(256) void k_append_quant(AppendParams p) {
   const int unit = gid >> 5;            // (row, block); whole half-waves share one unit
   const int e = gid & 31;               // element inside the block
   if (unit >= p.n_units) return;
-  const int row = unit / nb;
-  const int b = unit - row * nb;
+  // the values first: their loads do not depend on the destination lookup
+  const int row_l = unit / nb;
+  const int b = unit - row_l * nb;
+  const size_t src = (size_t)row_l * p.head_dim + b * kBlock + e;
+  const float xk = p.k_new[src];
+  const float xv = p.v_new[src];
+  // a wave holds two consecutive units of one row (nb is even), so the row
+  // and its destination are uniform and come from scalar loads
+  const int row = __builtin_amdgcn_readfirstlane(row_l);
   const int h = row % p.n_kv_heads;
   const int j = (row / p.n_kv_heads) % p.n_new;
   const int seq = row / (p.n_kv_heads * p.n_new);
@@ -66,11 +75,9 @@ __global__ __launch_bounds__(256) void k_append_quant(AppendParams p) {
   const size_t tile0 = prow & ~(size_t)(kTile - 1);   // first row of this token's 32-token tile
   const int t = (int)(prow - tile0);
 
-  const size_t src = (size_t)row * p.head_dim + b * kBlock + e;
-
   // ---- K: a = max|x|, d = fp16(a / 127), c = clamp(rne(x / d), -127, 127)
   {
-    const float x = p.k_new[src];
+    const float x = xk;
     const float a = max32(fabsf(x));
     const uint16_t dbits = f32_to_half_bits(a / 127.0f);
     const float d = half_bits_to_f32(dbits);
@@ -79,7 +86,7 @@ __global__ __launch_bounds__(256) void k_append_quant(AppendParams p) {
   }
 
   // ---- V
-  const float x = p.v_new[src];
+  const float x = xv;
   if (p.v_format == 0) {
     // q4_0: m = first element of largest magnitude, d = fp16(m / -8),
     // n = clamp(rne(x / d) + 8, 0, 15); byte j of the block = n_j | n_{j+16} << 4
