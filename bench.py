@@ -301,7 +301,8 @@ def main() -> int:
     torch.cuda.synchronize()
     attn_ms = np.array([a.elapsed_time(b) for a, b in evs])
 
-    # warm cache: one replica, so most of it stays in the 256 MB Infinity Cache
+    # one replica reused every step (with nontemporal K/V loads little of it
+    # stays in the 256 MB Infinity Cache)
     for i in range(args.warmup):
         step(0)
     w0 = torch.cuda.Event(enable_timing=True)
@@ -372,7 +373,8 @@ def main() -> int:
         "read_ceiling_gbs": read_gbs,
         "warm_single_replica": {"us_per_step": round(warm_ms * 1e3, 2),
                                 "gbs": round(nbytes["step"] / (warm_ms * 1e-3) / 1e9, 1),
-                                "note": "one cache replica, mostly resident in the Infinity Cache"},
+                                "note": "one cache replica reused every step; the K/V loads are "
+                                        "nontemporal, so little of it stays in the Infinity Cache"},
     }
     print(f"[bench] timed: {ms_step * 1e3:.2f} us/step, attention {attn_ms.mean() * 1e3:.2f} us",
           file=sys.stderr, flush=True)

@@ -61,36 +61,37 @@ __global__ __launch_bounds__(64) void k_debug_isum(const uint32_t* k_qs, const f
   }
 }
 
-// Plain streaming read of a buffer with 16-byte loads, eight per thread in
-// flight: the HBM read ceiling the attention kernels are measured against.
-// Each work-group reads whole 32 KB segments in turn; the xor of the data is
-// stored only in the unlikely case that it equals a sentinel, so the loads
-// cannot be dropped.
-__global__ __launch_bounds__(256) void k_debug_stream_read(const uint4* src, size_t n16,
+// Plain streaming read of a buffer with 16-byte nontemporal loads, eight per
+// thread in flight: the HBM read ceiling the attention kernels are measured
+// against (they read the K/V stream with the same hint).  Each work-group
+// reads one contiguous span; the xor of the data is stored only in the
+// unlikely case that it equals a sentinel, so the loads cannot be dropped.
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void k_debug_stream_read(const v4u* src, size_t n16,
                                                            uint32_t* sink) {
   constexpr int U = 8;
-  const size_t seg = (size_t)256 * U;
+  const size_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const size_t b0 = per * blockIdx.x;
+  const size_t b1 = b0 + per < n16 ? b0 + per : n16;
   uint32_t acc = 0;
-  for (size_t base = (size_t)blockIdx.x * seg; base < n16; base += (size_t)gridDim.x * seg) {
-    if (base + seg <= n16) {
-      uint4 v[U];
+  size_t base = b0;
+  for (; base + (size_t)256 * U <= b1; base += (size_t)256 * U) {
+    v4u v[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) v[u] = src[base + u * 256 + threadIdx.x];
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(src + base + u * 256 + threadIdx.x);
 #pragma unroll
-      for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
-    } else {
-      for (size_t i = base + threadIdx.x; i < n16; i += 256) {
-        const uint4 x = src[i];
-        acc ^= x.x ^ x.y ^ x.z ^ x.w;
-      }
-    }
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (size_t i = base + threadIdx.x; i < b1; i += 256) {
+    const v4u x = __builtin_nontemporal_load(src + i);
+    acc ^= x.x ^ x.y ^ x.z ^ x.w;
   }
   if (acc == 0x9E3779B9u) sink[0] = acc;
 }
 
 int launch_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream) {
-  hipLaunchKernelGGL(k_debug_stream_read, dim3(2048), dim3(256), 0, stream,
-                     static_cast<const uint4*>(buf), bytes / 16, sink);
+  hipLaunchKernelGGL(k_debug_stream_read, dim3(1024), dim3(256), 0, stream,
+                     static_cast<const v4u*>(buf), bytes / 16, sink);
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
