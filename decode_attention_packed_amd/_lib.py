@@ -24,8 +24,10 @@ KVQ_V_Q8_0 = 1
 KVQ_BLOCK = 32
 KVQ_SEG_ALIGN = 64
 KVQ_MAX_QTOK = 16
+KVQ_MAX_APPEND = 16
 
 EXPORTS = ("kvq_abi_version", "kvq_status_string", "kvq_cache_bytes", "kv_append_quant",
+           "attn_decode_packed_append",
            "attn_decode_packed_workspace_size", "attn_decode_packed", "kvq_debug_quant_q",
            "kvq_debug_qk_isum", "kvq_debug_stream_read")
 
@@ -69,6 +71,11 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_packed.argtypes = [P, c_void_p, c_void_p, c_int, c_int, c_int, c_void_p, c_int,
                                          c_void_p, c_int, c_float, c_int, c_void_p, c_size_t,
                                          c_void_p]
+        L.attn_decode_packed_append.restype = c_int
+        L.attn_decode_packed_append.argtypes = [P, c_void_p, c_void_p, c_void_p, c_void_p, c_int,
+                                                c_int, c_int, c_int, c_void_p, c_int, c_void_p,
+                                                c_int, c_float, c_int, c_void_p, c_size_t,
+                                                c_void_p]
         L.kvq_debug_stream_read.restype = c_int
         L.kvq_debug_stream_read.argtypes = [c_void_p, ctypes.c_size_t, c_void_p, c_void_p]
         L.kvq_debug_quant_q.restype = c_int
@@ -213,6 +220,41 @@ def attn_decode_packed(cache: PackedKVCache, q, out, seq_len, max_seq_len: int, 
                                     int(max_seq_len), float(sm_scale), int(bool(causal)),
                                     _ptr(workspace), ws_bytes, _stream(stream)),
            "attn_decode_packed")
+
+
+def attn_decode_packed_append(cache: PackedKVCache, q, k_new, v_new, out, seq_len,
+                              max_seq_len: int, sm_scale: float, causal: bool, workspace,
+                              seg_table=None, max_segs: int | None = None, stream=None) -> None:
+    """Append k_new / v_new (float32 [n_seq][n_new][n_kv_heads][head_dim]) at
+    tokens seq_len - n_new .. seq_len - 1 and attend, in one launch; other
+    arguments as attn_decode_packed."""
+    import torch
+    _need(q, torch.float32, "q", 4)
+    _need(out, torch.float32, "out", 4)
+    _need(k_new, torch.float32, "k_new", 4)
+    _need(v_new, torch.float32, "v_new", 4)
+    _need(seq_len, torch.int32, "seq_len", 1)
+    if q.shape != out.shape:
+        raise ValueError("q and out differ in shape")
+    if k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new differ in shape")
+    n_seq, n_qtok, n_q_heads, d = q.shape
+    if (d != cache.head_dim or seq_len.shape[0] != n_seq or k_new.shape[0] != n_seq
+            or k_new.shape[2] != cache.n_kv_heads or k_new.shape[3] != d):
+        raise ValueError("shape does not match the cache")
+    n_new = k_new.shape[1]
+    if seg_table is not None:
+        _need(seg_table, torch.int32, "seg_table", 2)
+        max_segs = seg_table.shape[1]
+    elif max_segs is None:
+        max_segs = cache.n_segs // n_seq
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().attn_decode_packed_append(ctypes.byref(cache.struct), _ptr(q), _ptr(k_new),
+                                           _ptr(v_new), _ptr(out), n_seq, n_qtok, n_q_heads, n_new,
+                                           _ptr(seg_table), int(max_segs), _ptr(seq_len),
+                                           int(max_seq_len), float(sm_scale), int(bool(causal)),
+                                           _ptr(workspace), ws_bytes, _stream(stream)),
+           "attn_decode_packed_append")
 
 
 def kvq_debug_stream_read(buf, sink, stream=None) -> None:

@@ -160,10 +160,12 @@ int attn_decode_packed_workspace_size(const kvq_cache* cache, int n_seq, int n_q
   return KVQ_OK;
 }
 
-int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n_seq, int n_qtok,
-                       int n_q_heads, const int32_t* seg_table, int max_segs,
-                       const int32_t* seq_len, int max_seq_len, float sm_scale, int causal,
-                       void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+int attn_common(const kvq_cache* cache, const float* q, float* out, int n_seq, int n_qtok,
+                int n_q_heads, const int32_t* seg_table, int max_segs, const int32_t* seq_len,
+                int max_seq_len, float sm_scale, int causal, void* workspace, size_t workspace_bytes,
+                const float* k_new, const float* v_new, int n_new, void* stream) {
   int st = check_attn(cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
                       max_seq_len);
   if (st) return st;
@@ -176,9 +178,35 @@ int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n
   if (workspace_bytes < need || !workspace) return KVQ_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KVQ_ERR_INVALID;
   const int r = kvq::launch_attn(*cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs,
-                                 seq_len, plan, sm_scale, causal ? 1 : 0, workspace,
-                                 static_cast<hipStream_t>(stream));
+                                 seq_len, plan, sm_scale, causal ? 1 : 0, workspace, k_new, v_new,
+                                 n_new, static_cast<hipStream_t>(stream));
   return r ? KVQ_ERR_HIP : KVQ_OK;
+}
+
+}  // namespace
+
+int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n_seq, int n_qtok,
+                       int n_q_heads, const int32_t* seg_table, int max_segs,
+                       const int32_t* seq_len, int max_seq_len, float sm_scale, int causal,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_common(cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
+                     max_seq_len, sm_scale, causal, workspace, workspace_bytes, nullptr, nullptr, 0,
+                     stream);
+}
+
+int attn_decode_packed_append(const kvq_cache* cache, const float* q, const float* k_new,
+                              const float* v_new, float* out, int n_seq, int n_qtok, int n_q_heads,
+                              int n_new, const int32_t* seg_table, int max_segs,
+                              const int32_t* seq_len, int max_seq_len, float sm_scale, int causal,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_INVALID;
+  if (n_new < 1 || n_new > KVQ_MAX_APPEND || n_new > max_seq_len) return KVQ_ERR_INVALID;
+  if (cache && n_seq > 0 &&
+      (long long)n_seq * n_new * cache->n_kv_heads * cache->head_dim > 0x7fffff00LL)
+    return KVQ_ERR_INVALID;
+  return attn_common(cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
+                     max_seq_len, sm_scale, causal, workspace, workspace_bytes, k_new, v_new, n_new,
+                     stream);
 }
 
 int kvq_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

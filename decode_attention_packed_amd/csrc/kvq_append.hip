@@ -35,20 +35,6 @@ struct AppendParams {
   int v_format;
 };
 
-// max / min over the 32 lanes of a half-wave: DPP inside each 16-lane row,
-// then one exchange between the two rows
-__device__ __forceinline__ float max32(float x) {
-  x = max_row16(x);
-  return fmaxf(x, shfl_xor_f(x, 16));
-}
-__device__ __forceinline__ int min32(int x) {
-  x = min(x, dpp_i<0xB1>(x));
-  x = min(x, dpp_i<0x4E>(x));
-  x = min(x, dpp_i<0x141>(x));
-  x = min(x, dpp_i<0x140>(x));
-  return min(x, __shfl_xor(x, 16));
-}
-
 __global__ __launch_bounds__(256) void k_append_quant(AppendParams p) {
   const int nb = p.head_dim / kBlock;
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
@@ -75,42 +61,24 @@ __global__ __launch_bounds__(256) void k_append_quant(AppendParams p) {
   const size_t tile0 = prow & ~(size_t)(kTile - 1);   // first row of this token's 32-token tile
   const int t = (int)(prow - tile0);
 
-  // ---- K: a = max|x|, d = fp16(a / 127), c = clamp(rne(x / d), -127, 127)
+  // ---- K
   {
-    const float x = xk;
-    const float a = max32(fabsf(x));
-    const uint16_t dbits = f32_to_half_bits(a / 127.0f);
-    const float d = half_bits_to_f32(dbits);
-    p.k_qs[prow * p.head_dim + b * kBlock + e] = (uint8_t)quant_code(x, d, -127.0f, 127.0f);
+    int code;
+    const uint16_t dbits = quant_sym8(xk, code);
+    p.k_qs[prow * p.head_dim + b * kBlock + e] = (uint8_t)code;
     if (e == 0) p.k_d[tile0 * nb + b * kTile + t] = dbits;
   }
 
   // ---- V
-  const float x = xv;
   if (p.v_format == 0) {
-    // q4_0: m = first element of largest magnitude, d = fp16(m / -8),
-    // n = clamp(rne(x / d) + 8, 0, 15); byte j of the block = n_j | n_{j+16} << 4
-    const float ax = fabsf(x);
-    const float a = max32(ax);
-    const int first = min32(ax == a ? e : kBlock);
-    const float m = __shfl(x, ((int)__lane_id() & 32) + first);
-    // fp16(m / -8) of m = +-0 is -+0.  The compiler contracts the scaling and
-    // the fp16 conversion into one fma with a +0 addend, which would turn -0
-    // into +0, so the zero case is spelled out.
-    const uint16_t dbits = (m == 0.0f) ? (signbit(m) ? (uint16_t)0x0000 : (uint16_t)0x8000)
-                                       : f32_to_half_bits(m / -8.0f);
-    const float d = half_bits_to_f32(dbits);
-    const int n = quant_code(x, d, -8.0f, 7.0f) + 8;
-    const int n_hi = __shfl_xor(n, 16);
-    if (e < 16)
-      p.v_qs[tile0 * (p.head_dim / 2) + (size_t)(b * 16 + e) * kTile + t] = (uint8_t)(n | (n_hi << 4));
+    uint32_t byte;
+    const uint16_t dbits = quant_q4_0(xv, e, byte);
+    if (e < 16) p.v_qs[tile0 * (p.head_dim / 2) + (size_t)(b * 16 + e) * kTile + t] = (uint8_t)byte;
     if (e == 0) p.v_d[tile0 * nb + b * kTile + t] = dbits;
   } else {
-    const float a = max32(fabsf(x));
-    const uint16_t dbits = f32_to_half_bits(a / 127.0f);
-    const float d = half_bits_to_f32(dbits);
-    p.v_qs[tile0 * p.head_dim + (size_t)(b * kBlock + e) * kTile + t] =
-        (uint8_t)quant_code(x, d, -127.0f, 127.0f);
+    int code;
+    const uint16_t dbits = quant_sym8(xv, code);
+    p.v_qs[tile0 * p.head_dim + (size_t)(b * kBlock + e) * kTile + t] = (uint8_t)code;
     if (e == 0) p.v_d[tile0 * nb + b * kTile + t] = dbits;
   }
 }

@@ -55,15 +55,19 @@ namespace kvq {
 constexpr int kWaves = 8;                  // one work-group fills a CU (two waves per SIMD)
 constexpr int kThreads = kWaves * 64;
 constexpr int kLdsBudget = 163840 - 512;   // LDS of one work-group, less the small shared words
+constexpr int kMaxAppend = KVQ_MAX_APPEND;  // appended tokens per sequence in one call
 
 typedef _Float16 v2h __attribute__((ext_vector_type(2)));
 
 struct AttnParams {
-  const uint32_t* k_qs;
-  const uint16_t* k_d;
-  const uint8_t* v_qs;
-  const uint16_t* v_d;
+  uint32_t* k_qs;
+  uint16_t* k_d;
+  uint8_t* v_qs;
+  uint16_t* v_d;
   const float* q;
+  const float* k_new;     // rows appended at the end of each sequence, [n_seq][n_new][n_kv][D]
+  const float* v_new;
+  int n_new;              // 0: attention only
   float* out;
   float* part_o;          // [n_seq][n_kv][n_split][rows][D]
   float* part_ml;         // [n_seq][n_kv][n_split][rows][2]
@@ -131,14 +135,24 @@ struct Slot {
   static constexpr int PBYTES = kRows * (kTile + 4) * 4;   // padded P staging tile (row layout)
   static constexpr bool P_IN_K = PBYTES <= KBYTES;   // P can reuse the K area
   static constexpr int PBUF = P_IN_K ? 0 : kWaves * PBYTES;   // row layout only
+  // packed bytes of one appended token in the patch buffer: K row, K scales,
+  // V row, V scales
+  static constexpr int PK = 0, PKS = D, PV = D + 2 * NB, PVS = D + 2 * NB + VROW;
+  static constexpr int PTOK = (PVS + 2 * NB + 15) & ~15;
+  static constexpr int PATCH = kMaxAppend * PTOK;   // patch buffer, after the ring
   // three slots per wave where they fit in the CU's LDS, else two
-  static constexpr int NSLOT = (3 * BYTES * kWaves + PBUF <= kLdsBudget) ? 3 : 2;
+  static constexpr int NSLOT = (3 * BYTES * kWaves + PBUF + PATCH <= kLdsBudget) ? 3 : 2;
   static constexpr int QSTAGE = 1024;                // fp32 Q rows of one wave (at most 1 KB)
+  // fp32 appended rows staged in a wave's last slot, behind the Q staging
+  // (and, in wave 0, the Q codes and scales)
+  static constexpr int STAGE = (QSTAGE + kRows * D + kRows * NB * 4 + 15) & ~15;
+  static constexpr int STAGE_UNITS = 2 * kMaxAppend / kWaves;   // rows per wave
   static constexpr int LPT = KBYTES / 1024 + VBYTES / 1024 + (SBYTES == 256 ? 2 : 1);   // loads per tile
   static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "whole 1 KB load steps");
   static_assert(kRows / kWaves * D * 4 <= QSTAGE && QSTAGE + kRows * D + kRows * NB * 4 <= BYTES,
                 "Q staging does not fit a slot");
-  static_assert(NSLOT * BYTES * kWaves + PBUF <= kLdsBudget, "ring does not fit the LDS");
+  static_assert(NSLOT * BYTES * kWaves + PBUF + PATCH <= kLdsBudget, "ring does not fit the LDS");
+  static_assert(STAGE + STAGE_UNITS * D * 4 <= BYTES, "appended rows do not fit a slot");
 };
 
 // Direct global->LDS loads (lane l's bytes land at lds + size * l for the
@@ -326,6 +340,147 @@ __device__ __forceinline__ void run_ring(const AttnParams& p, int seq, int kvh, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Rows appended in the same call
+// ---------------------------------------------------------------------------
+//
+// With n_new > 0 the call first appends the rows k_new / v_new at tokens
+// L - n_new .. L - 1 of each sequence, exactly as kv_append_quant does, and
+// then attends over all L tokens.  The work-group whose chunk holds such a
+// token stages the fp32 rows in its prologue (ahead of its tiles), quantizes
+// them with the append kernel's block quantizers into a patch buffer in LDS,
+// patches every tile it loads that holds one of them (the cache still holds
+// the old rows), and writes the packed rows to the cache at the end.
+
+// Appended tokens [lo, hi) that fall into this work-group's chunk [c0, c1).
+struct AppendRange {
+  int lo, hi;
+};
+__device__ __forceinline__ AppendRange append_range(const AttnParams& p, int L, int c0, int c1) {
+  AppendRange a;
+  a.lo = max(c0, L - p.n_new);
+  a.hi = p.n_new > 0 ? c1 : c0;
+  if (a.lo > a.hi) a.lo = a.hi;
+  return a;
+}
+
+// Stage this wave's appended rows (unit u = 2 * token + {0: K, 1: V}, units
+// wave, wave + kWaves, ...) as fp32 in its last slot, one dword per lane.
+template <int D, int VF>
+__device__ __forceinline__ void stage_appended(const AttnParams& p, int seq, int kvh, int L, int wave,
+                                               const AppendRange& a, uint32_t stage_lds) {
+  using S = Slot<D, VF>;
+  const int units = 2 * (a.hi - a.lo);
+#pragma unroll
+  for (int i = 0; i < S::STAGE_UNITS; ++i) {
+    const int u = wave + kWaves * i;
+    if (u >= units) break;
+    const int j = a.lo + (u >> 1) - (L - p.n_new);   // row of k_new / v_new
+    const float* src = ((u & 1) ? p.v_new : p.k_new) +
+                       (((size_t)seq * p.n_new + j) * p.n_kv_heads + kvh) * D;
+#pragma unroll
+    for (int n = 0; n < D / 64; ++n) dma4_v(src + 64 * n + __lane_id(), stage_lds + i * D * 4 + 256 * n);
+  }
+}
+
+// Quantize this wave's staged rows into the patch buffer (per token: K row,
+// K scales, V row, V scales, as the append kernel computes them).
+template <int D, int VF>
+__device__ __forceinline__ void quantize_appended(const AppendRange& a, int wave, const float* stage,
+                                                  uint8_t* patch) {
+  using S = Slot<D, VF>;
+  const int lane = __lane_id();
+  const int e = lane & 31;
+  const int units = 2 * (a.hi - a.lo);
+#pragma unroll
+  for (int i = 0; i < S::STAGE_UNITS; ++i) {
+    const int u = wave + kWaves * i;
+    if (u >= units) break;
+    uint8_t* pt = patch + (u >> 1) * S::PTOK;
+#pragma unroll
+    for (int e0 = 0; e0 < D; e0 += 64) {
+      const float x = stage[i * D + e0 + lane];
+      const int b = (e0 + lane) / kBlock;
+      int code;
+      uint32_t byte;
+      if (!(u & 1)) {
+        const uint16_t dbits = quant_sym8(x, code);
+        pt[S::PK + e0 + lane] = (uint8_t)code;
+        if (e == 0) reinterpret_cast<uint16_t*>(pt + S::PKS)[b] = dbits;
+      } else if (VF == 0) {
+        const uint16_t dbits = quant_q4_0(x, e, byte);
+        if (e < 16) pt[S::PV + b * 16 + e] = (uint8_t)byte;
+        if (e == 0) reinterpret_cast<uint16_t*>(pt + S::PVS)[b] = dbits;
+      } else {
+        const uint16_t dbits = quant_sym8(x, code);
+        pt[S::PV + e0 + lane] = (uint8_t)code;
+        if (e == 0) reinterpret_cast<uint16_t*>(pt + S::PVS)[b] = dbits;
+      }
+    }
+  }
+}
+
+// Overwrite the appended tokens of tile t0 in its ring slot with their
+// packed rows, in the slot's layout (K rows swizzled in 16-byte chunks, V
+// and both scale planes token-interleaved).
+template <int D, int VF>
+__device__ __forceinline__ void patch_tile(uint8_t* slot, const uint8_t* patch, int t0,
+                                           const AppendRange& a) {
+  using S = Slot<D, VF>;
+  constexpr int NB = D / kBlock;
+  const int lane = __lane_id();
+  const int lo = max(t0, a.lo), hi = min(t0 + kTile, a.hi);
+  for (int pos = lo; pos < hi; ++pos) {
+    const int r = pos - t0;
+    const uint8_t* pt = patch + (pos - a.lo) * S::PTOK;
+    if (lane < D / 4) {
+      const int q = lane >> 2;
+      *reinterpret_cast<uint32_t*>(slot + S::K_OFF + (r * S::CPR + (q ^ (r % S::CPR))) * 16 + 4 * (lane & 3)) =
+          reinterpret_cast<const uint32_t*>(pt + S::PK)[lane];
+    }
+#pragma unroll
+    for (int k0 = 0; k0 < S::VROW; k0 += 64) {
+      const int k = k0 + lane;
+      if (k < S::VROW) slot[S::V_OFF + (2 * k + ((r >> 4) ^ ((k >> 2) & 1))) * 16 + (r & 15)] = pt[S::PV + k];
+    }
+    if (lane < NB) {
+      reinterpret_cast<uint16_t*>(slot + S::DK_OFF)[lane * kTile + r] =
+          reinterpret_cast<const uint16_t*>(pt + S::PKS)[lane];
+      reinterpret_cast<uint16_t*>(slot + S::DV_OFF)[lane * kTile + r] =
+          reinterpret_cast<const uint16_t*>(pt + S::PVS)[lane];
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Write the packed appended rows of this work-group to the cache (the
+// layout kv_append_quant writes).  Runs after the work-group's loads.
+template <int D, int VF>
+__device__ __forceinline__ void write_appended(const AttnParams& p, int seq, int kvh,
+                                               const AppendRange& a, const uint8_t* patch) {
+  using S = Slot<D, VF>;
+  constexpr int NB = D / kBlock;
+  const int tid = threadIdx.x;
+  for (int pos = a.lo; pos < a.hi; ++pos) {
+    const uint8_t* pt = patch + (pos - a.lo) * S::PTOK;
+    const int segj = pos / p.seg_tokens;
+    const int seg = segment_of(p.seg_table, seq, p.max_segs, segj);
+    const size_t prow = ((size_t)seg * p.n_kv_heads + kvh) * p.seg_tokens + (pos - segj * p.seg_tokens);
+    const size_t tile0 = prow & ~(size_t)(kTile - 1);
+    const int t = (int)(prow - tile0);
+    uint8_t* kq = reinterpret_cast<uint8_t*>(p.k_qs);
+    if (tid < D / 4)
+      reinterpret_cast<uint32_t*>(kq + prow * D)[tid] = reinterpret_cast<const uint32_t*>(pt + S::PK)[tid];
+    for (int k = tid; k < S::VROW; k += kThreads) p.v_qs[tile0 * S::VROW + (size_t)k * kTile + t] = pt[S::PV + k];
+    if (tid < NB) {
+      p.k_d[tile0 * NB + tid * kTile + t] = reinterpret_cast<const uint16_t*>(pt + S::PKS)[tid];
+      p.v_d[tile0 * NB + tid * kTile + t] = reinterpret_cast<const uint16_t*>(pt + S::PVS)[tid];
+    }
+  }
+}
+
 // Common prologue: this wave's Q rows (wave, wave + kWaves) go to its last
 // slot as fp32 ahead of its first tiles, so waiting for them leaves the tiles
 // in flight; then they are quantized (a = max|q|, d = a / 127 in fp32) into
@@ -335,7 +490,8 @@ __device__ __forceinline__ void run_ring(const AttnParams& p, int seq, int kvh, 
 // publishes the codes.
 template <int D, int VF>
 __device__ __forceinline__ void prologue(const AttnParams& p, uint8_t* s_lds, int seq, int kvh,
-                                         int wave, int c1, const TileLane<D, VF>& tl,
+                                         int wave, int L, int c1, const AppendRange& app,
+                                         uint8_t* s_patch, const TileLane<D, VF>& tl,
                                          TileCursor& cur, const TileQueue& q, int8_t*& s_qc,
                                          float*& s_qd) {
   using S = Slot<D, VF>;
@@ -357,6 +513,9 @@ __device__ __forceinline__ void prologue(const AttnParams& p, uint8_t* s_lds, in
                        4 * (pc % (D / 4));
     dma16_v(src, ring_lds + (NSLOT - 1) * S::BYTES);
   }
+  // appended rows, ahead of the tiles so that waiting for them leaves the
+  // tiles in flight
+  if (app.hi > app.lo) stage_appended<D, VF>(p, seq, kvh, L, wave, app, ring_lds + (NSLOT - 1) * S::BYTES + S::STAGE);
   const int n_pro = (q.cur < c1) + (NSLOT == 3 && q.n1 < c1);
   if (q.cur < c1) issue_tile<D, VF>(p, seq, kvh, q.cur, ring_lds, tl, cur);
   if (NSLOT == 3 && q.n1 < c1) issue_tile<D, VF>(p, seq, kvh, q.n1, ring_lds + S::BYTES, tl, cur);
@@ -377,6 +536,9 @@ __device__ __forceinline__ void prologue(const AttnParams& p, uint8_t* s_lds, in
 #pragma unroll
     for (int e = 0; e < D / 64; ++e) quantize_q_lane(qv[k][e], 64 * e + lane, s_qc + r * D, s_qd + r * NB);
   }
+  if (app.hi > app.lo)
+    quantize_appended<D, VF>(app, wave, reinterpret_cast<const float*>(ring + (NSLOT - 1) * S::BYTES + S::STAGE),
+                             s_patch);
   __syncthreads();
 }
 
@@ -750,7 +912,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_rows(AttnParams p) {
   constexpr int NT = D / 16;
   constexpr int RING = kWaves * S::NSLOT * S::BYTES + S::PBUF;
   constexpr int MERGE = kWaves * kRows * D * 4 + 2 * kWaves * kRows * 4;
-  constexpr int LDS_BYTES = RING > MERGE ? RING : MERGE;
+  static_assert(MERGE <= RING, "the merge buffer overlaps the patch buffer");
+  constexpr int LDS_BYTES = RING + S::PATCH;
 
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   __shared__ int s_last;
@@ -776,7 +939,9 @@ __global__ __launch_bounds__(kThreads) void k_attn_rows(AttnParams p) {
 
   int8_t* s_qc;
   float* s_qd;
-  prologue<D, VF>(p, s_lds, seq, kvh, wave, c1, tl, cur, tq, s_qc, s_qd);
+  const AppendRange app = append_range(p, L, c0, c1);
+  uint8_t* s_patch = s_lds + RING;
+  prologue<D, VF>(p, s_lds, seq, kvh, wave, L, c1, app, s_patch, tl, cur, tq, s_qc, s_qd);
   long qa[NB];
   load_q_operands<D>(s_qc, qa);
   float dqs[4][NB];
@@ -805,9 +970,11 @@ __global__ __launch_bounds__(kThreads) void k_attn_rows(AttnParams p) {
   float* pbuf = reinterpret_cast<float*>(s_lds + kWaves * S::NSLOT * S::BYTES + wave * S::PBYTES);
   auto body = [&](auto slot_c, int t0) {
     constexpr int SL = decltype(slot_c)::value;
+    if (t0 + kTile > app.lo && t0 < app.hi) patch_tile<D, VF>(ring + SL * S::BYTES, s_patch, t0, app);
     process_tile<D, VF>(ring + SL * S::BYTES, pbuf, t0, c1, qa, dqs, vis, st);
   };
   run_ring<D, VF>(p, seq, kvh, c0, c1, &s_next, ring_lds, tl, cur, tq, body);
+  if (app.hi > app.lo) write_appended<D, VF>(p, seq, kvh, app, s_patch);
 
   // ---- this wave's rows to LDS for the merge
   float* s_buf = reinterpret_cast<float*>(s_lds);
@@ -985,7 +1152,8 @@ __global__ __launch_bounds__(kThreads) void k_attn_cols(AttnParams p) {
   constexpr int NG = D / 16;
   constexpr int RING = kWaves * S::NSLOT * S::BYTES;
   constexpr int MERGE = kWaves * kRows * D * 4 + 2 * kWaves * kRows * 4;
-  constexpr int LDS_BYTES = RING > MERGE ? RING : MERGE;
+  static_assert(MERGE <= RING, "the merge buffer overlaps the patch buffer");
+  constexpr int LDS_BYTES = RING + S::PATCH;
 
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   __shared__ int s_last;
@@ -1011,7 +1179,9 @@ __global__ __launch_bounds__(kThreads) void k_attn_cols(AttnParams p) {
 
   int8_t* s_qc;
   float* s_qd;
-  prologue<D, VF>(p, s_lds, seq, kvh, wave, c1, tl, cur, tq, s_qc, s_qd);
+  const AppendRange app = append_range(p, L, c0, c1);
+  uint8_t* s_patch = s_lds + RING;
+  prologue<D, VF>(p, s_lds, seq, kvh, wave, L, c1, app, s_patch, tl, cur, tq, s_qc, s_qd);
 
   // column (row r, block b); B operands hold row r's Q codes of block bb in
   // the columns of block bb only
@@ -1035,15 +1205,17 @@ __global__ __launch_bounds__(kThreads) void k_attn_cols(AttnParams p) {
   st.c0 = (b == 0 && !valid) ? -1e30f : 0.0f;
   st.l = 0.0f;
 
-  const uint8_t* ring = s_lds + wave * S::NSLOT * S::BYTES;
+  uint8_t* ring = s_lds + wave * S::NSLOT * S::BYTES;
   bool first = true;
   auto body = [&](auto slot_c, int t0) {
     constexpr int SL = decltype(slot_c)::value;
+    if (t0 + kTile > app.lo && t0 < app.hi) patch_tile<D, VF>(ring + SL * S::BYTES, s_patch, t0, app);
     process_tile_cols<D, VF>(ring + SL * S::BYTES, t0, c1, t0 + kTile <= vis_min, first, vis, valid,
                              qb, wq, st);
     first = false;
   };
   run_ring<D, VF>(p, seq, kvh, c0, c1, &s_next, ring_lds, tl, cur, tq, body);
+  if (app.hi > app.lo) write_appended<D, VF>(p, seq, kvh, app, s_patch);
 
   // ---- this wave's rows to LDS for the merge
   float* s_buf = reinterpret_cast<float*>(s_lds);
@@ -1087,7 +1259,7 @@ static void launch_attn_kernel(const AttnParams& p, dim3 grid, hipStream_t strea
 int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
                 const int32_t* seg_table, int max_segs, const int32_t* seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
-                hipStream_t stream) {
+                const float* k_new, const float* v_new, int n_new, hipStream_t stream) {
   AttnParams p;
   const WorkspaceLayout ws = workspace_layout(c, n_seq, n_qtok, n_q_heads, plan);
   char* base = static_cast<char*>(workspace);
@@ -1096,6 +1268,9 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
   p.v_qs = c.v_qs;
   p.v_d = c.v_d;
   p.q = q;
+  p.k_new = k_new;
+  p.v_new = v_new;
+  p.n_new = n_new;
   p.out = out;
   p.counters = reinterpret_cast<unsigned*>(base + ws.counters);
   p.part_o = reinterpret_cast<float*>(base + ws.part_o);

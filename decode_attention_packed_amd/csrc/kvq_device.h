@@ -69,6 +69,54 @@ __device__ __forceinline__ float sum_row16(float x) {
   return x;
 }
 
+// Max / min over the 32 lanes of a half-wave: DPP inside each 16-lane row,
+// then one exchange between the two rows.
+__device__ __forceinline__ float half_max(float x) {
+  x = max_row16(x);
+  return fmaxf(x, shfl_xor_f(x, 16));
+}
+__device__ __forceinline__ int half_min(int x) {
+  x = min(x, dpp_i<0xB1>(x));
+  x = min(x, dpp_i<0x4E>(x));
+  x = min(x, dpp_i<0x141>(x));
+  x = min(x, dpp_i<0x140>(x));
+  return min(x, __shfl_xor(x, 16));
+}
+
+// Block quantization of the cache formats (page 1: int8 K payload with an
+// fp16 scale per 32-block; V as q4_0 or q8_0).  The 32 lanes of a half-wave
+// hold the 32 elements of one block, lane e element e.
+//
+// Symmetric int8 (K and q8_0 V): a = max|x|, d = fp16(a / 127),
+// c = clamp(rne(x / d), -127, 127).  Returns the scale bits.
+__device__ __forceinline__ uint16_t quant_sym8(float x, int& code) {
+  const float a = half_max(fabsf(x));
+  const uint16_t dbits = f32_to_half_bits(a / 127.0f);
+  const float d = half_bits_to_f32(dbits);
+  code = quant_code(x, d, -127.0f, 127.0f);
+  return dbits;
+}
+
+// q4_0: m = first element of largest magnitude, d = fp16(m / -8),
+// n = clamp(rne(x / d) + 8, 0, 15).  Returns the scale bits; `byte` is
+// n_e | n_{e+16} << 4, the block's byte e, on lanes e < 16.
+__device__ __forceinline__ uint16_t quant_q4_0(float x, int e, uint32_t& byte) {
+  const float ax = fabsf(x);
+  const float a = half_max(ax);
+  const int first = half_min(ax == a ? e : kBlock);
+  const float m = __shfl(x, ((int)__lane_id() & 32) + first);
+  // fp16(m / -8) of m = +-0 is -+0.  The compiler contracts the scaling and
+  // the fp16 conversion into one fma with a +0 addend, which would turn -0
+  // into +0, so the zero case is spelled out.
+  const uint16_t dbits = (m == 0.0f) ? (signbit(m) ? (uint16_t)0x0000 : (uint16_t)0x8000)
+                                     : f32_to_half_bits(m / -8.0f);
+  const float d = half_bits_to_f32(dbits);
+  const int n = quant_code(x, d, -8.0f, 7.0f) + 8;
+  const int n_hi = __shfl_xor(n, 16);
+  byte = (uint32_t)(n | (n_hi << 4));
+  return dbits;
+}
+
 // One element of Q quantization: x is element `idx` of a row of blocks, and
 // the 32 lanes of this half-wave hold the 32 elements of its block.  Per
 // 32-block a = max|x|, d = a / 127 kept in fp32, codes as quant_code.

@@ -39,11 +39,13 @@ int launch_append(const kvq_cache& c, const float* k_new, const float* v_new, in
 
 bool attn_supported(int head_dim, int v_format);
 
-// Split-K attention with the split merge fused into the last work-group.
+// Split-K attention with the split merge fused into the last work-group;
+// with n_new > 0 it first appends k_new / v_new at tokens seq_len - n_new ..
+// seq_len - 1 of every sequence (in the same launch).
 int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
                 const int32_t* seg_table, int max_segs, const int32_t* seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
-                hipStream_t stream);
+                const float* k_new, const float* v_new, int n_new, hipStream_t stream);
 
 int launch_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 int launch_debug_quant_q(const float* q, int n_rows, int head_dim, int8_t* codes, float* scales,

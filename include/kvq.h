@@ -39,6 +39,7 @@ extern "C" {
 #define KVQ_BLOCK 32            /* elements per quantization block along head_dim */
 #define KVQ_SEG_ALIGN 64        /* seg_tokens must be a positive multiple of this */
 #define KVQ_MAX_QTOK 16         /* query tokens x query heads per kv head, at most */
+#define KVQ_MAX_APPEND 16       /* tokens one fused append-and-attend call appends per sequence */
 
 enum kvq_status {
   KVQ_OK = 0,
@@ -151,6 +152,30 @@ int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n
                        int n_qtok, int n_q_heads, const int32_t* seg_table, int max_segs,
                        const int32_t* seq_len, int max_seq_len, float sm_scale, int causal,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_packed_append: one decode step that first appends new rows and
+ * then attends, in a single launch.  The result (cache contents and output)
+ * is that of kv_append_quant with start_pos[i] = seq_len[i] - n_new followed
+ * by attn_decode_packed with the same arguments: page 1 re-packs each new
+ * K row as it is written and attends over the packed cache, and the decode
+ * step appends the token it attends from.
+ *   k_new, v_new  device float [n_seq][n_new][n_kv_heads][head_dim], written
+ *                 at tokens seq_len[i] - n_new .. seq_len[i] - 1
+ *   n_new         1 .. KVQ_MAX_APPEND, and n_new <= seq_len[i] for every i
+ *                 (n_new = n_qtok with causal set is the verify step: the
+ *                 draft tokens are appended and each query sees the tokens
+ *                 up to its own)
+ * All other arguments, the workspace and the errors are those of
+ * attn_decode_packed.  The appended rows are written once the work-group
+ * that holds them has read its part of the cache, so they need not be in
+ * the cache beforehand.
+ */
+int attn_decode_packed_append(const kvq_cache* cache, const float* q, const float* k_new,
+                              const float* v_new, float* out, int n_seq, int n_qtok,
+                              int n_q_heads, int n_new, const int32_t* seg_table, int max_segs,
+                              const int32_t* seq_len, int max_seq_len, float sm_scale,
+                              int causal, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Test hooks: expose the integer stages of the hot path so they can be

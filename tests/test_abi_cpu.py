@@ -112,3 +112,25 @@ def test_bad_append_args_rejected():
     assert f(ctypes.byref(c), 0x1000, 0x2000, 1, 1, None, 1, 0x3002, None) == K.KVQ_ERR_INVALID
     assert f(ctypes.byref(_fake_cache(head_dim=256)), 0x1000, 0x2000, 1, 1, None, 1, 0x3000,
              None) == K.KVQ_ERR_UNSUPPORTED
+
+
+def test_bad_fused_append_args_rejected():
+    c = _fake_cache()
+    L = K.lib()
+
+    def call(k_new=0x9000, v_new=0xA000, n_new=1, **kw):
+        a = dict(q=0x5000, out=0x6000, n_seq=1, n_qtok=1, hq=32, table=None, max_segs=1,
+                 seq_len=0x7000, max_len=1024, scale=0.1, ws=0x8000, ws_bytes=1 << 30)
+        a.update(kw)
+        return L.attn_decode_packed_append(ctypes.byref(c), a["q"], k_new, v_new, a["out"],
+                                           a["n_seq"], a["n_qtok"], a["hq"], n_new, a["table"],
+                                           a["max_segs"], a["seq_len"], a["max_len"], a["scale"], 0,
+                                           a["ws"], a["ws_bytes"], None)
+
+    assert call(k_new=None) == K.KVQ_ERR_INVALID
+    assert call(v_new=0xA004) == K.KVQ_ERR_INVALID            # misaligned
+    assert call(n_new=0) == K.KVQ_ERR_INVALID
+    assert call(n_new=K.KVQ_MAX_APPEND + 1) == K.KVQ_ERR_INVALID
+    assert call(n_new=4, max_len=2) == K.KVQ_ERR_INVALID      # more new rows than tokens
+    assert call(hq=12) == K.KVQ_ERR_INVALID                   # the attention checks still apply
+    assert call(ws_bytes=16) == K.KVQ_ERR_WORKSPACE
