@@ -52,7 +52,10 @@
 
 namespace kvq {
 
-constexpr int kWaves = 8;                  // one work-group fills a CU (two waves per SIMD)
+#ifndef KVQ_WAVES
+#define KVQ_WAVES 8
+#endif
+constexpr int kWaves = KVQ_WAVES;          // one work-group fills a CU
 constexpr int kThreads = kWaves * 64;
 constexpr int kLdsBudget = 163840 - 512;   // LDS of one work-group, less the small shared words
 constexpr int kMaxAppend = KVQ_MAX_APPEND;  // appended tokens per sequence in one call
@@ -146,10 +149,10 @@ struct Slot {
   // fp32 appended rows staged in a wave's last slot, behind the Q staging
   // (and, in wave 0, the Q codes and scales)
   static constexpr int STAGE = (QSTAGE + kRows * D + kRows * NB * 4 + 15) & ~15;
-  static constexpr int STAGE_UNITS = 2 * kMaxAppend / kWaves;   // rows per wave
+  static constexpr int STAGE_UNITS = (2 * kMaxAppend + kWaves - 1) / kWaves;   // rows per wave
   static constexpr int LPT = KBYTES / 1024 + VBYTES / 1024 + (SBYTES == 256 ? 2 : 1);   // loads per tile
   static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "whole 1 KB load steps");
-  static_assert(kRows / kWaves * D * 4 <= QSTAGE && QSTAGE + kRows * D + kRows * NB * 4 <= BYTES,
+  static_assert((kRows + kWaves - 1) / kWaves * D * 4 <= QSTAGE && QSTAGE + kRows * D + kRows * NB * 4 <= BYTES,
                 "Q staging does not fit a slot");
   static_assert(NSLOT * BYTES * kWaves + PBUF + PATCH <= kLdsBudget, "ring does not fit the LDS");
   static_assert(STAGE + STAGE_UNITS * D * 4 <= BYTES, "appended rows do not fit a slot");
@@ -196,8 +199,21 @@ __device__ __forceinline__ int load_uniform(const int32_t* ptr) {
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
-// Per-lane byte offsets of one tile's loads inside its global rows.  The K
-// swizzle and the V chunk order repeat every 1 KB.
+// K rows are stored in LDS with their 16-byte chunks permuted: chunk q of
+// token row t sits at chunk q ^ kswz(t) of the row.  The column layout reads
+// 8 bytes per lane from 16 rows (tokens 8a + 4h + c for a, c < 4) and two
+// chunks at once; folding both a and c into the permutation spreads those
+// reads evenly over the LDS banks (XOR with t % 8 alone left half of them
+// idle and doubled the cycles of every K read).
+template <int CPR>
+__device__ __forceinline__ int kswz(int t) {
+  if constexpr (CPR == 8) return (2 * ((t ^ (t >> 3)) & 3)) | ((t >> 2) & 1);
+  else return (t ^ (t >> 3)) & 3;
+}
+
+// Per-lane byte offsets of one tile's loads inside its global rows (lane l
+// of load n fills LDS chunk l of that load's 1 KB).  The V chunk order
+// repeats every 1 KB.
 template <int D, int VF>
 struct TileLane {
   uint32_t k[Slot<D, VF>::KBYTES / 1024];
@@ -209,11 +225,14 @@ __device__ __forceinline__ TileLane<D, VF> tile_lane_offsets(int lane) {
   using S = Slot<D, VF>;
   TileLane<D, VF> t;
   const int r = lane / S::CPR;
-  const int q = (lane % S::CPR) ^ (r % S::CPR);
   const int R = lane >> 1;
   const int c = (lane & 1) ^ ((R >> 2) & 1);
+  constexpr int ROWS_PER_KB = 1024 / D;
 #pragma unroll
-  for (int n = 0; n < S::KBYTES / 1024; ++n) t.k[n] = (uint32_t)(r * D + 16 * q + 1024 * n);
+  for (int n = 0; n < S::KBYTES / 1024; ++n) {
+    const int q = (lane % S::CPR) ^ kswz<S::CPR>(r + ROWS_PER_KB * n);
+    t.k[n] = (uint32_t)(r * D + 16 * q + 1024 * n);
+  }
 #pragma unroll
   for (int n = 0; n < S::VBYTES / 1024; ++n) t.v[n] = (uint32_t)(R * 32 + 16 * c + 1024 * n);
   t.s = (uint32_t)(4 * (lane % (S::SBYTES / 4)));
@@ -228,7 +247,7 @@ struct TileCursor {
 };
 
 // Issue the loads of one tile (32 tokens starting at t0) into a ring slot.
-// K rows (CPR chunks) land at chunk r*CPR + (q ^ (r % CPR)); V rows (two
+// K rows (CPR chunks) land at chunk r*CPR + (q ^ kswz(r)); V rows (two
 // chunks) at R*2 + (c ^ ((R >> 2) & 1)); scale planes as they are.
 template <int D, int VF>
 __device__ __forceinline__ void issue_tile(const AttnParams& p, int seq, int kvh, int t0,
@@ -435,7 +454,7 @@ __device__ __forceinline__ void patch_tile(uint8_t* slot, const uint8_t* patch, 
     const uint8_t* pt = patch + (pos - a.lo) * S::PTOK;
     if (lane < D / 4) {
       const int q = lane >> 2;
-      *reinterpret_cast<uint32_t*>(slot + S::K_OFF + (r * S::CPR + (q ^ (r % S::CPR))) * 16 + 4 * (lane & 3)) =
+      *reinterpret_cast<uint32_t*>(slot + S::K_OFF + (r * S::CPR + (q ^ kswz<S::CPR>(r))) * 16 + 4 * (lane & 3)) =
           reinterpret_cast<const uint32_t*>(pt + S::PK)[lane];
     }
 #pragma unroll
@@ -497,7 +516,7 @@ __device__ __forceinline__ void prologue(const AttnParams& p, uint8_t* s_lds, in
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
   constexpr int NSLOT = S::NSLOT;
-  constexpr int RPW = kRows / kWaves;   // Q rows per wave
+  constexpr int RPW = (kRows + kWaves - 1) / kWaves;   // Q rows per wave
   constexpr int PIECES = RPW * D / 4;   // 16-byte pieces of them
   static_assert(PIECES <= 64, "one load per wave");
   const int lane = __lane_id();
@@ -533,6 +552,7 @@ __device__ __forceinline__ void prologue(const AttnParams& p, uint8_t* s_lds, in
 #pragma unroll
   for (int k = 0; k < RPW; ++k) {
     const int r = wave + kWaves * k;
+    if (r >= kRows) break;
 #pragma unroll
     for (int e = 0; e < D / 64; ++e) quantize_q_lane(qv[k][e], 64 * e + lane, s_qc + r * D, s_qd + r * NB);
   }
@@ -666,7 +686,7 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, 
 
   // split maxima and sums first (wave w takes rows w, w + kWaves, one lane
   // per split), then the first batch of partial outputs, all in flight at once
-  constexpr int kRowsPerWave = kRows / kWaves;
+  constexpr int kRowsPerWave = (kRows + kWaves - 1) / kWaves;
   float2 ml[kRowsPerWave];
 #pragma unroll
   for (int k = 0; k < kRowsPerWave; ++k) {
@@ -790,7 +810,7 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const int q = 2 * b + (grp >> 1);
-      kb[b] = *reinterpret_cast<const long*>(slot + S::K_OFF + (r * S::CPR + (q ^ (r % S::CPR))) * 16 +
+      kb[b] = *reinterpret_cast<const long*>(slot + S::K_OFF + (r * S::CPR + (q ^ kswz<S::CPR>(r))) * 16 +
                                              8 * (grp & 1));
     }
     _Float16 dk[NB];   // scale b of token r sits at slot b*32 + r
@@ -1048,7 +1068,7 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
     for (int bb = 0; bb < NB; ++bb) {
       const int q = 2 * bb + (grp >> 1);
       const long ka = *reinterpret_cast<const long*>(
-          slot + S::K_OFF + (tau * S::CPR + (q ^ (tau % S::CPR))) * 16 + 8 * (grp & 1));
+          slot + S::K_OFF + (tau * S::CPR + (q ^ kswz<S::CPR>(tau))) * 16 + 8 * (grp & 1));
       cq[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ka, qb[bb], cq[h], 0, 0, 0);
     }
   }
