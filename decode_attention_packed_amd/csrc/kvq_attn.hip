@@ -706,13 +706,9 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, 
   for (int k = 0; k < kRowsPerWave; ++k) {
     const int rr = wave + kWaves * k;
     if (rr >= R) break;
-    float M = ml[k].x;
-#pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) M = fmaxf(M, shfl_xor_f(M, sh));
+    const float M = wave_max(ml[k].x);
     const float e = lane < nsp ? __builtin_amdgcn_exp2f(ml[k].x - M) : 0.0f;
-    float den = e * ml[k].y;
-#pragma unroll
-    for (int sh = 1; sh < 64; sh <<= 1) den += shfl_xor_f(den, sh);
+    const float den = wave_sum(e * ml[k].y);
     if (lane < nsp) sw[lane * R + rr] = e / den;
   }
   __syncthreads();
@@ -1094,8 +1090,7 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
   if (!valid) mx = -INFINITY;
   if (first || __any(mx > 0.0f)) {
     // row maximum over the four lane groups (the block lanes agree already)
-    float rm = fmaxf(mx, shfl_xor_f(mx, 16));
-    rm = fmaxf(rm, shfl_xor_f(rm, 32));
+    const float rm = across32(across16(mx, fmax2), fmax2);
     float delta;
     if (first) {
       delta = rm == -INFINITY ? 0.0f : rm;   // nothing accumulated yet
@@ -1241,9 +1236,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_cols(AttnParams p) {
   float* s_buf = reinterpret_cast<float*>(s_lds);
   float* s_m = s_buf + kWaves * kRows * D;
   float* s_l = s_m + kWaves * kRows;
-  float l = st.l;
-  l += shfl_xor_f(l, 16);
-  l += shfl_xor_f(l, 32);
+  const float l = across32(across16(st.l, fadd), fadd);
   __syncthreads();   // every wave is done with its ring
   if (valid) {
     // q4_0 high-nibble dims (odd g) were accumulated 16 times too large

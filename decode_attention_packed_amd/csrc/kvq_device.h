@@ -53,6 +53,29 @@ __device__ __forceinline__ float shfl_xor_f(float x, int mask) {
       float, __builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __builtin_bit_cast(int, x)));
 }
 
+// Exchanges between rows of 16 lanes without LDS (gfx950 lane swaps).  With
+// both registers holding x, v_permlane16_swap leaves x of the even rows in the
+// first and x of the odd rows in the second, in every lane, so combining the
+// two applies op to (x, x ^ 16); v_permlane32_swap does the same for the two
+// halves of the wave, (x, x ^ 32).  Issued from inline assembly: the
+// compiler's builtin for these swaps reads the first result's register for
+// both results once they meet in one arithmetic operation.  The s_nop covers
+// the wait states between a VALU write and the swap's read.
+template <class Op>
+__device__ __forceinline__ float across16(float x, Op op) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return op(a, b);
+}
+template <class Op>
+__device__ __forceinline__ float across32(float x, Op op) {
+  float a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  return op(a, b);
+}
+__device__ __forceinline__ float fadd(float a, float b) { return a + b; }
+__device__ __forceinline__ float fmax2(float a, float b) { return fmaxf(a, b); }
+
 // Max / sum over the 16 lanes of a DPP row (lane ^ 1, ^ 2, mirror in 8, mirror in 16).
 __device__ __forceinline__ float max_row16(float x) {
   x = fmaxf(x, dpp_f<0xB1>(x));
@@ -72,8 +95,14 @@ __device__ __forceinline__ float sum_row16(float x) {
 // Max / min over the 32 lanes of a half-wave: DPP inside each 16-lane row,
 // then one exchange between the two rows.
 __device__ __forceinline__ float half_max(float x) {
-  x = max_row16(x);
-  return fmaxf(x, shfl_xor_f(x, 16));
+  return across16(max_row16(x), fmax2);
+}
+// Max / sum over all 64 lanes of a wave, in every lane.
+__device__ __forceinline__ float wave_max(float x) {
+  return across32(across16(max_row16(x), fmax2), fmax2);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  return across32(across16(sum_row16(x), fadd), fadd);
 }
 __device__ __forceinline__ int half_min(int x) {
   x = min(x, dpp_i<0xB1>(x));
@@ -121,12 +150,7 @@ __device__ __forceinline__ uint16_t quant_q4_0(float x, int e, uint32_t& byte) {
 // the 32 lanes of this half-wave hold the 32 elements of its block.  Per
 // 32-block a = max|x|, d = a / 127 kept in fp32, codes as quant_code.
 __device__ __forceinline__ void quantize_q_lane(float x, int idx, int8_t* codes, float* scales) {
-  float a = fabsf(x);
-  a = fmaxf(a, shfl_xor_f(a, 1));
-  a = fmaxf(a, shfl_xor_f(a, 2));
-  a = fmaxf(a, shfl_xor_f(a, 4));
-  a = fmaxf(a, shfl_xor_f(a, 8));
-  a = fmaxf(a, shfl_xor_f(a, 16));
+  const float a = half_max(fabsf(x));
   const float d = a / 127.0f;
   codes[idx] = (int8_t)quant_code(x, d, -127.0f, 127.0f);
   if ((idx & 31) == 0) scales[idx / kBlock] = d;
