@@ -365,8 +365,11 @@ def main() -> int:
 
     nbytes = algorithmic_bytes(spec, L, 1)
     gbs = nbytes["step"] / (ms_step * 1e-3) / 1e9
-    attn_mean_s = float(attn_ms.mean()) * 1e-3
-    achieved = nbytes["step"] / attn_mean_s / 1e9
+    # The step is one launch, so the kernel's average launch duration is the
+    # timed region (events on the launch stream around all K launches) over K.
+    # Per-step event pairs (kernel_us) add their own packets between launches
+    # and read ~2 us longer; they are kept for the spread.
+    achieved = nbytes["step"] / (ms_step * 1e-3) / 1e9
     result = {
         "metric": "decode attention µs/step + KV GB/s (% of HBM peak) at 128k ctx, 1 GPU",
         "value": round(gbs, 1),
@@ -389,7 +392,8 @@ def main() -> int:
         "two_launch": {"us_per_step": round(two_launch_ms * 1e3, 2),
                        "gbs": round(nbytes["step"] / (two_launch_ms * 1e-3) / 1e9, 1),
                        "note": "kv_append_quant then attn_decode_packed, same work"},
-        "kernel_us": {"mean": round(float(attn_ms.mean()) * 1e3, 2),
+        "kernel_us": {"note": "per-step event pairs around each launch (they add their own gaps)",
+                      "mean": round(float(attn_ms.mean()) * 1e3, 2),
                     "p10": round(float(np.percentile(attn_ms, 10)) * 1e3, 2),
                     "p50": round(float(np.percentile(attn_ms, 50)) * 1e3, 2),
                     "p90": round(float(np.percentile(attn_ms, 90)) * 1e3, 2)},
