@@ -170,6 +170,12 @@ int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n
  * attn_decode_packed.  The appended rows are written once the work-group
  * that holds them has read its part of the cache, so they need not be in
  * the cache beforehand.
+ *
+ * Speculative accept / rollback: after a verify step that appended n draft
+ * rows, accepting k of them needs no call and moves no data.  The caller's
+ * length becomes seq_len[i] - n + k; rows past it are never read, and the
+ * next call appends over them.  The same holds for a plain rewind of a
+ * sequence to any shorter length.
  */
 int attn_decode_packed_append(const kvq_cache* cache, const float* q, const float* k_new,
                               const float* v_new, float* out, int n_seq, int n_qtok,
