@@ -179,6 +179,84 @@ def algorithmic_bytes(spec, n_tokens: int, append_rows: int) -> dict:
     return {"attn": attn, "append": app, "step": attn + app, "per_token_head": kb + vb}
 
 
+def _build_cache(K, torch, ci):
+    """One packed cache holding every sequence of `ci`, filled by bulk
+    kv_append_quant through each sequence's segment list."""
+    spec = ci.spec
+    cache = K.PackedKVCache(spec.n_kv_heads, spec.head_dim, ci.seg_tokens, ci.n_segs, spec.v_format)
+    if ci.seg_table is not None:
+        table = torch.from_numpy(ci.seg_table).cuda()
+    else:
+        per = ci.n_segs // spec.n_seq
+        table = torch.arange(ci.n_segs, dtype=torch.int32).view(spec.n_seq, per).cuda()
+    zero = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for i in range(spec.n_seq):
+        n = int(ci.seq_len[i])
+        k = ci.k[i] if isinstance(ci.k, list) else ci.k[i, :n]
+        v = ci.v[i] if isinstance(ci.v, list) else ci.v[i, :n]
+        K.kv_append_quant(cache, torch.from_numpy(np.ascontiguousarray(k[None])).cuda(),
+                          torch.from_numpy(np.ascontiguousarray(v[None])).cuda(), zero,
+                          seg_table=table[i:i + 1])
+    return cache, table
+
+
+def other_configs(K, W, torch, stream, steps: int, warmup: int) -> list:
+    """The other workloads, each step the attention calls its recipe
+    defines (no append): tiny, gqa8k in both V formats, the verify step
+    (main and draft caches, two calls on one stream) and the ragged batch.
+    Enough cache replicas rotate that one pass touches more than the 256 MB
+    Infinity Cache, except for tiny (106 KB), which is latency-bound."""
+    rows = []
+    plans = [("tiny", ["tiny"], 1), ("gqa8k_q4_0", ["gqa8k_q4_0"], 24), ("gqa8k_q8_0", ["gqa8k_q8_0"], 18),
+             ("verify128k", ["main", "draft"], 2), ("ragged", ["ragged"], 2)]
+    inputs = {}
+    for wl in ("tiny", "gqa8k", "verify128k", "ragged"):
+        for ci in W.make_inputs(wl):
+            inputs[ci.spec.name] = ci
+    for label, names, reps in plans:
+        calls = []
+        nbytes = 0
+        for nm in names:
+            ci = inputs[nm]
+            spec = ci.spec
+            built = [_build_cache(K, torch, ci) for _ in range(reps)]
+            q = torch.from_numpy(ci.q).cuda()
+            out = torch.empty_like(q)
+            sl = torch.from_numpy(ci.seq_len).cuda()
+            mx = int(ci.seq_len.max())
+            ws = torch.zeros(max(16, K.attn_decode_packed_workspace_size(
+                built[0][0], spec.n_seq, spec.n_qtok, spec.n_q_heads, mx)), dtype=torch.uint8,
+                device="cuda")
+            calls.append((built, q, out, sl, mx, spec, ws))
+            per = algorithmic_bytes(spec, 1, 0)["per_token_head"]
+            nbytes += int(ci.seq_len.astype(np.int64).sum()) * spec.n_kv_heads * per
+        torch.cuda.synchronize()
+
+        def run(i):
+            for built, q, out, sl, mx, spec, ws in calls:
+                cache, table = built[i % len(built)]
+                K.attn_decode_packed(cache, q, out, sl, mx, spec.sm_scale, spec.causal, ws,
+                                     seg_table=table, stream=stream)
+        for i in range(warmup):
+            run(i)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            run(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        rows.append({"workload": label, "us_per_step": round(ms * 1e3, 2), "kv_bytes_per_step": nbytes,
+                     "gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
+                     "launches_per_step": len(names), "replicas": reps})
+        print(f"[bench] {label}: {ms * 1e3:.2f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+        del calls
+        torch.cuda.empty_cache()
+    return rows
+
+
 def cpu_baseline(ci, target_s: float = 12.0) -> dict:
     """The oracle on the host: the same step (quantize the new token into
     the packed cache, then attention over all tokens from the packed cache),
@@ -218,6 +296,8 @@ def main() -> int:
     ap.add_argument("--replicas", type=int, default=3)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-other-configs", action="store_true",
+                    help="skip the timing of the other workloads (tiny, gqa8k, verify128k, ragged)")
     ap.add_argument("--calibrate", action="store_true",
                     help="also run the known-size read and copy kernels (for counter runs)")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "CMD"),
@@ -408,6 +488,11 @@ def main() -> int:
     }
     print(f"[bench] timed: {ms_step * 1e3:.2f} us/step, attention {attn_ms.mean() * 1e3:.2f} us",
           file=sys.stderr, flush=True)
+    if not args.no_other_configs:
+        del caches
+        torch.cuda.empty_cache()
+        result["other_configs"] = other_configs(K, W, torch, stream, max(50, args.steps // 5),
+                                                max(10, args.warmup // 4))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(ci, args.cpu_seconds)
     print(json.dumps(result), flush=True)
