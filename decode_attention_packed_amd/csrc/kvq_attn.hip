@@ -89,6 +89,7 @@ struct AttnParams {
   int causal;
   float scale_log2;       // sm_scale * log2(e)
   int xcd_local;          // splits of a (sequence, kv head) share an XCD (see block_coords)
+  int merge_launch;       // 1: the split merge runs as a second launch (k_split_merge)
 };
 
 // Work-groups go to the 8 XCDs round-robin by linear index.  When the number
@@ -648,7 +649,8 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, 
                          __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (single) return;
+  // with the merge as its own launch, the kernel boundary publishes the partials
+  if (single || p.merge_launch) return;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // The counter's low 16 bits count finished splits; each work-group that is
@@ -942,7 +944,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_rows(AttnParams p) {
   const BlockCoords bc = block_coords(p);
   const int split = bc.split, kvh = bc.kvh, seq = bc.seq;
   const int L = p.seq_len[seq];
-  const int n_split_seq = (L + p.chunk - 1) / p.chunk;
+  const int n_split_seq = min((L + p.chunk - 1) / p.chunk, p.n_split);   // clamp: see k_split_merge
   if (split >= n_split_seq) return;
   const int c0 = split * p.chunk;
   const int c1 = min(c0 + p.chunk, L);
@@ -1181,7 +1183,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_cols(AttnParams p) {
   const BlockCoords bc = block_coords(p);
   const int split = bc.split, kvh = bc.kvh, seq = bc.seq;
   const int L = p.seq_len[seq];
-  const int n_split_seq = (L + p.chunk - 1) / p.chunk;
+  const int n_split_seq = min((L + p.chunk - 1) / p.chunk, p.n_split);   // clamp: see k_split_merge
   if (split >= n_split_seq) return;
   const int c0 = split * p.chunk;
   const int c1 = min(c0 + p.chunk, L);
@@ -1257,16 +1259,76 @@ __global__ __launch_bounds__(kThreads) void k_attn_cols(AttnParams p) {
   finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq, bc.off_xcd);
 }
 
+// ---------------------------------------------------------------------------
+// Split merge as its own launch
+// ---------------------------------------------------------------------------
+//
+// For the row layout (up to 16 query rows) a split's partial is 16 rows of D
+// floats, and one work-group reading every split's partial would be limited
+// by its own CU's bandwidth (hundreds of KB for 32-64 splits).  There the
+// attention kernel only stores the partials, and this kernel combines them
+// with one 64-lane work-group per (sequence, kv head, row): lane s holds
+// split s's maximum and sum, the weights exp2(m_s - M) / sum_s exp2(m_s - M)
+// l_s go through LDS, and each lane combines D/64 columns of the row.
+template <int D>
+__global__ __launch_bounds__(64) void k_split_merge(AttnParams p) {
+  constexpr int C = D / 64;   // columns per lane
+  __shared__ float s_w[kMaxSplits];
+  const int lane = threadIdx.x;
+  const int R = p.rows, G = p.group;
+  const int r = blockIdx.x % R;
+  const int grp = blockIdx.x / R;   // sequence * n_kv_heads + kv head
+  const int seq = grp / p.n_kv_heads, kvh = grp - seq * p.n_kv_heads;
+  const int L = p.seq_len[seq];
+  // (seq_len above max_seq_len breaks the call's contract; the clamp keeps
+  // the reads inside this group's partials even then)
+  const int nsp = min((L + p.chunk - 1) / p.chunk, p.n_split);
+  if (nsp <= 1) return;   // a single split wrote its rows itself
+  const size_t pbase = (size_t)grp * p.n_split;
+  float m = -INFINITY, l = 0.0f;
+  if (lane < nsp) {
+    const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + ((pbase + lane) * R + r) * 2);
+    m = ml.x;
+    l = ml.y;
+  }
+  const float M = wave_max(m);
+  const float e = lane < nsp ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
+  const float den = wave_sum(e * l);
+  if (lane < nsp) s_w[lane] = e / den;
+  __syncthreads();
+  const float* ob = p.part_o + (pbase * R + r) * D + C * lane;
+  float acc[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) acc[c] = 0.0f;
+#pragma unroll 8
+  for (int sp = 0; sp < nsp; ++sp) {
+    const float w = s_w[sp];
+    const float* src = ob + (size_t)sp * R * D;
+#pragma unroll
+    for (int c = 0; c < C; ++c) acc[c] = fmaf(w, src[c], acc[c]);
+  }
+  float* dst = p.out + (((size_t)seq * p.n_qtok + r / G) * p.n_q_heads + kvh * G + r % G) * D + C * lane;
+#pragma unroll
+  for (int c = 0; c < C; ++c) dst[c] = acc[c];
+}
+
 bool attn_supported(int head_dim, int v_format) {
   return (head_dim == 64 || head_dim == 128) && (v_format == 0 || v_format == 1);
 }
 
 template <int D, int VF>
-static void launch_attn_kernel(const AttnParams& p, dim3 grid, hipStream_t stream) {
-  if (p.rows * (D / kBlock) <= 16)
+static void launch_attn_kernel(AttnParams p, dim3 grid, hipStream_t stream) {
+  if (p.rows * (D / kBlock) <= 16) {
+    p.merge_launch = 0;
     hipLaunchKernelGGL((k_attn_cols<D, VF>), grid, dim3(kThreads), 0, stream, p);
-  else
+  } else {
+    p.merge_launch = p.n_split > 1;
     hipLaunchKernelGGL((k_attn_rows<D, VF>), grid, dim3(kThreads), 0, stream, p);
+    if (p.merge_launch) {
+      const long long n_groups = grid.x / p.n_split;
+      hipLaunchKernelGGL((k_split_merge<D>), dim3((unsigned)(n_groups * p.rows)), dim3(64), 0, stream, p);
+    }
+  }
 }
 
 int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
