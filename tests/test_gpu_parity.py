@@ -158,6 +158,19 @@ def test_attention_parity(name):
         H.assert_close(got, ref, ci.spec.name)
 
 
+@pytest.mark.parametrize("chunk", [1024, 4096])
+def test_attention_ragged_forced_splits(chunk, monkeypatch):
+    """The ragged batch with the split size forced small, so its long
+    sequences cross many splits and segments (its default plan keeps at most
+    two splits per sequence, the batch being wide enough to fill the GPU)."""
+    monkeypatch.setenv("KVQ_CHUNK_TOKENS", str(chunk))
+    ci = W.make_inputs("ragged")[0]
+    _say(f"attention ragged, {chunk}-token splits")
+    cache, table, max_segs = H.build_cache(ci)
+    got = H.run_attention(cache, ci, table, max_segs)
+    H.assert_close(got, H.oracle_attention(ci), f"ragged chunk {chunk}")
+
+
 def test_attention_parity_long128k_step():
     """The long-context step at full size: append one token at the last
     position, then attend over all 131072 tokens; the oracle checks the
