@@ -29,7 +29,8 @@ KVQ_MAX_APPEND = 16
 EXPORTS = ("kvq_abi_version", "kvq_status_string", "kvq_cache_bytes", "kv_append_quant",
            "attn_decode_packed_append",
            "attn_decode_packed_workspace_size", "attn_decode_packed", "kvq_debug_quant_q",
-           "kvq_debug_qk_isum", "kvq_debug_stream_read")
+           "kvq_debug_qk_isum", "kvq_debug_stream_read", "kvq_f16k_cache_bytes", "kv_append_f16k",
+           "attn_decode_f16k_workspace_size", "attn_decode_f16k")
 
 
 class KvqCacheStruct(ctypes.Structure):
@@ -76,6 +77,14 @@ def lib() -> ctypes.CDLL:
                                                 c_int, c_int, c_int, c_void_p, c_int, c_void_p,
                                                 c_int, c_float, c_int, c_void_p, c_size_t,
                                                 c_void_p]
+        L.kvq_f16k_cache_bytes.restype = c_int
+        L.kvq_f16k_cache_bytes.argtypes = [c_int, c_int, c_int, c_int, c_int, POINTER(c_size_t)]
+        L.kv_append_f16k.restype = c_int
+        L.kv_append_f16k.argtypes = L.kv_append_quant.argtypes
+        L.attn_decode_f16k_workspace_size.restype = c_int
+        L.attn_decode_f16k_workspace_size.argtypes = L.attn_decode_packed_workspace_size.argtypes
+        L.attn_decode_f16k.restype = c_int
+        L.attn_decode_f16k.argtypes = L.attn_decode_packed.argtypes
         L.kvq_debug_stream_read.restype = c_int
         L.kvq_debug_stream_read.argtypes = [c_void_p, ctypes.c_size_t, c_void_p, c_void_p]
         L.kvq_debug_quant_q.restype = c_int
@@ -163,10 +172,73 @@ class PackedKVCache:
         return sum(t.numel() * t.element_size() for t in (self.k_qs, self.k_d, self.v_qs, self.v_d))
 
 
+class F16KCache:
+    """The fp16-K A/B cache: K as binary16 rows [n_segs][n_kv_heads][seg_tokens]
+    [head_dim] (no K scales), V as in PackedKVCache.  head_dim 128 only."""
+
+    def __init__(self, n_kv_heads: int, head_dim: int, seg_tokens: int, n_segs: int,
+                 v_format: int, device="cuda"):
+        import torch
+        k, kd, vq, vd = kvq_f16k_cache_bytes(n_kv_heads, head_dim, seg_tokens, n_segs, v_format)
+        nb = head_dim // KVQ_BLOCK
+        shape = (n_segs, n_kv_heads, seg_tokens)
+        self.k = torch.empty(shape + (head_dim,), dtype=torch.int16, device=device)
+        vrow = head_dim // 2 if v_format == KVQ_V_Q4_0 else head_dim
+        self.v_qs = torch.empty(shape + (vrow,), dtype=torch.uint8, device=device)
+        self.v_d = torch.empty(shape + (nb,), dtype=torch.int16, device=device)
+        assert (self.k.numel() * 2, kd, self.v_qs.numel(), self.v_d.numel() * 2) == (k, 0, vq, vd)
+        self.n_kv_heads, self.head_dim, self.seg_tokens = n_kv_heads, head_dim, seg_tokens
+        self.n_segs, self.v_format = n_segs, v_format
+        self.struct = KvqCacheStruct(n_kv_heads, head_dim, seg_tokens, n_segs, v_format, 0,
+                                     self.k.data_ptr(), None, self.v_qs.data_ptr(),
+                                     self.v_d.data_ptr())
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.k, self.v_qs, self.v_d))
+
+
+def kvq_f16k_cache_bytes(n_kv_heads: int, head_dim: int, seg_tokens: int, n_segs: int,
+                         v_format: int) -> tuple:
+    out = (c_size_t * 4)()
+    _check(lib().kvq_f16k_cache_bytes(n_kv_heads, head_dim, seg_tokens, n_segs, v_format, out),
+           "kvq_f16k_cache_bytes")
+    return tuple(int(x) for x in out)
+
+
+def kv_append_f16k(cache: F16KCache, k_new, v_new, start_pos, seg_table=None,
+                   max_segs: int | None = None, stream=None) -> None:
+    """kv_append_quant for the fp16-K A/B cache."""
+    _append(lib().kv_append_f16k, "kv_append_f16k", cache, k_new, v_new, start_pos, seg_table,
+            max_segs, stream)
+
+
+def attn_decode_f16k_workspace_size(cache: F16KCache, n_seq: int, n_qtok: int, n_q_heads: int,
+                                    max_seq_len: int) -> int:
+    out = c_size_t(0)
+    _check(lib().attn_decode_f16k_workspace_size(ctypes.byref(cache.struct), n_seq, n_qtok,
+                                                 n_q_heads, max_seq_len, ctypes.byref(out)),
+           "attn_decode_f16k_workspace_size")
+    return int(out.value)
+
+
+def attn_decode_f16k(cache: F16KCache, q, out, seq_len, max_seq_len: int, sm_scale: float,
+                     causal: bool, workspace, seg_table=None, max_segs: int | None = None,
+                     stream=None) -> None:
+    """attn_decode_packed for the fp16-K A/B cache (Q rounded to fp16)."""
+    _attend(lib().attn_decode_f16k, "attn_decode_f16k", cache, q, out, seq_len, max_seq_len,
+            sm_scale, causal, workspace, seg_table, max_segs, stream)
+
+
 def kv_append_quant(cache: PackedKVCache, k_new, v_new, start_pos, seg_table=None,
                     max_segs: int | None = None, stream=None) -> None:
     """k_new, v_new: float32 [n_seq][n_new][n_kv_heads][head_dim] on the GPU;
     start_pos: int32 [n_seq]; seg_table: int32 [n_seq][max_segs] or None."""
+    _append(lib().kv_append_quant, "kv_append_quant", cache, k_new, v_new, start_pos, seg_table,
+            max_segs, stream)
+
+
+def _append(fn, where, cache, k_new, v_new, start_pos, seg_table, max_segs, stream) -> None:
     import torch
     _need(k_new, torch.float32, "k_new", 4)
     _need(v_new, torch.float32, "v_new", 4)
@@ -181,9 +253,8 @@ def kv_append_quant(cache: PackedKVCache, k_new, v_new, start_pos, seg_table=Non
         max_segs = seg_table.shape[1]
     elif max_segs is None:
         max_segs = cache.n_segs // n_seq
-    _check(lib().kv_append_quant(ctypes.byref(cache.struct), _ptr(k_new), _ptr(v_new), n_seq, n_new,
-                                 _ptr(seg_table), int(max_segs), _ptr(start_pos), _stream(stream)),
-           "kv_append_quant")
+    _check(fn(ctypes.byref(cache.struct), _ptr(k_new), _ptr(v_new), n_seq, n_new,
+              _ptr(seg_table), int(max_segs), _ptr(start_pos), _stream(stream)), where)
 
 
 def attn_decode_packed_workspace_size(cache: PackedKVCache, n_seq: int, n_qtok: int,
@@ -200,6 +271,12 @@ def attn_decode_packed(cache: PackedKVCache, q, out, seq_len, max_seq_len: int, 
                        stream=None) -> None:
     """q, out: float32 [n_seq][n_qtok][n_q_heads][head_dim]; seq_len: int32 [n_seq];
     workspace: a GPU tensor of at least attn_decode_packed_workspace_size bytes."""
+    _attend(lib().attn_decode_packed, "attn_decode_packed", cache, q, out, seq_len, max_seq_len,
+            sm_scale, causal, workspace, seg_table, max_segs, stream)
+
+
+def _attend(fn, where, cache, q, out, seq_len, max_seq_len, sm_scale, causal, workspace, seg_table,
+            max_segs, stream) -> None:
     import torch
     _need(q, torch.float32, "q", 4)
     _need(out, torch.float32, "out", 4)
@@ -215,11 +292,9 @@ def attn_decode_packed(cache: PackedKVCache, q, out, seq_len, max_seq_len: int, 
     elif max_segs is None:
         max_segs = cache.n_segs // n_seq
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().attn_decode_packed(ctypes.byref(cache.struct), _ptr(q), _ptr(out), n_seq, n_qtok,
-                                    n_q_heads, _ptr(seg_table), int(max_segs), _ptr(seq_len),
-                                    int(max_seq_len), float(sm_scale), int(bool(causal)),
-                                    _ptr(workspace), ws_bytes, _stream(stream)),
-           "attn_decode_packed")
+    _check(fn(ctypes.byref(cache.struct), _ptr(q), _ptr(out), n_seq, n_qtok, n_q_heads,
+              _ptr(seg_table), int(max_segs), _ptr(seq_len), int(max_seq_len), float(sm_scale),
+              int(bool(causal)), _ptr(workspace), ws_bytes, _stream(stream)), where)
 
 
 def attn_decode_packed_append(cache: PackedKVCache, q, k_new, v_new, out, seq_len,

@@ -15,15 +15,18 @@ namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-int check_cache(const kvq_cache* c) {
+// f16k: the fp16-K A/B cache (k_qs holds fp16 K rows, k_d must be NULL,
+// head_dim 128 only).
+int check_cache(const kvq_cache* c, bool f16k = false) {
   if (!c) return KVQ_ERR_INVALID;
   if (c->n_kv_heads < 1 || c->n_segs < 1 || c->reserved != 0) return KVQ_ERR_INVALID;
   if (c->seg_tokens < KVQ_SEG_ALIGN || c->seg_tokens % KVQ_SEG_ALIGN) return KVQ_ERR_INVALID;
   if (c->v_format != KVQ_V_Q4_0 && c->v_format != KVQ_V_Q8_0) return KVQ_ERR_INVALID;
   if (c->head_dim < KVQ_BLOCK || c->head_dim % KVQ_BLOCK) return KVQ_ERR_INVALID;
-  if (c->head_dim != 64 && c->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
-  if (!c->k_qs || !c->k_d || !c->v_qs || !c->v_d) return KVQ_ERR_INVALID;
-  if (!aligned16(c->k_qs) || !aligned16(c->k_d) || !aligned16(c->v_qs) || !aligned16(c->v_d))
+  if (c->head_dim != 128 && (f16k || c->head_dim != 64)) return KVQ_ERR_UNSUPPORTED;
+  if (!c->k_qs || !c->v_qs || !c->v_d || (f16k ? c->k_d != nullptr : !c->k_d)) return KVQ_ERR_INVALID;
+  if (!aligned16(c->k_qs) || (!f16k && !aligned16(c->k_d)) || !aligned16(c->v_qs) ||
+      !aligned16(c->v_d))
     return KVQ_ERR_INVALID;
   return KVQ_OK;
 }
@@ -38,8 +41,8 @@ int check_segments(const kvq_cache* c, int n_seq, const int32_t* seg_table, int 
 
 int check_attn(const kvq_cache* c, const float* q, const float* out, int n_seq, int n_qtok,
                int n_q_heads, const int32_t* seg_table, int max_segs, const int32_t* seq_len,
-               int max_seq_len) {
-  int st = check_cache(c);
+               int max_seq_len, bool f16k = false) {
+  int st = check_cache(c, f16k);
   if (st) return st;
   if (!q || !out || !seq_len || !aligned16(q) || !aligned16(out)) return KVQ_ERR_INVALID;
   if (reinterpret_cast<uintptr_t>(seq_len) & 3u) return KVQ_ERR_INVALID;
@@ -216,6 +219,66 @@ int attn_decode_packed_append(const kvq_cache* cache, const float* q, const floa
   return attn_common(cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
                      max_seq_len, sm_scale, causal, workspace, workspace_bytes, k_new, v_new, n_new,
                      stream);
+}
+
+int kvq_f16k_cache_bytes(int n_kv_heads, int head_dim, int seg_tokens, int n_segs, int v_format,
+                         size_t out_bytes[4]) {
+  const int st = kvq_cache_bytes(n_kv_heads, head_dim, seg_tokens, n_segs, v_format, out_bytes);
+  if (st) return st;
+  out_bytes[0] *= 2;   // fp16 K rows
+  out_bytes[1] = 0;    // no K scales
+  return KVQ_OK;
+}
+
+int kv_append_f16k(const kvq_cache* cache, const float* k_new, const float* v_new, int n_seq,
+                   int n_new, const int32_t* seg_table, int max_segs, const int32_t* start_pos,
+                   void* stream) {
+  int st = check_cache(cache, true);
+  if (st) return st;
+  if (!k_new || !v_new || !start_pos || !aligned16(k_new) || !aligned16(v_new)) return KVQ_ERR_INVALID;
+  if (reinterpret_cast<uintptr_t>(start_pos) & 3u) return KVQ_ERR_INVALID;
+  if (n_seq < 1 || n_new < 1) return KVQ_ERR_INVALID;
+  if ((long long)n_seq * n_new * cache->n_kv_heads * cache->head_dim > 0x7fffff00LL)
+    return KVQ_ERR_INVALID;
+  st = check_segments(cache, n_seq, seg_table, max_segs);
+  if (st) return st;
+  const int r = kvq::launch_append(*cache, k_new, v_new, n_seq, n_new, seg_table, max_segs,
+                                   start_pos, static_cast<hipStream_t>(stream), true);
+  return r ? KVQ_ERR_HIP : KVQ_OK;
+}
+
+int attn_decode_f16k_workspace_size(const kvq_cache* cache, int n_seq, int n_qtok, int n_q_heads,
+                                    int max_seq_len, size_t* bytes) {
+  if (!bytes) return KVQ_ERR_INVALID;
+  int st = check_cache(cache, true);
+  if (st) return st;
+  if (n_seq < 1 || n_qtok < 1 || n_q_heads < 1 || n_q_heads % cache->n_kv_heads || max_seq_len < 1)
+    return KVQ_ERR_INVALID;
+  const kvq::SplitPlan plan = kvq::plan_splits(*cache, n_seq, n_qtok, n_q_heads, max_seq_len);
+  *bytes = kvq::workspace_layout(*cache, n_seq, n_qtok, n_q_heads, plan).total;
+  return KVQ_OK;
+}
+
+int attn_decode_f16k(const kvq_cache* cache, const float* q, float* out, int n_seq, int n_qtok,
+                     int n_q_heads, const int32_t* seg_table, int max_segs, const int32_t* seq_len,
+                     int max_seq_len, float sm_scale, int causal, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_attn(cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
+                      max_seq_len, true);
+  if (st) return st;
+  if (!std::isfinite(sm_scale)) return KVQ_ERR_INVALID;
+  // column layout only: query rows of a kv group times 4 blocks fill at most 16 MFMA columns
+  if (n_qtok * (n_q_heads / cache->n_kv_heads) * (cache->head_dim / KVQ_BLOCK) > 16)
+    return KVQ_ERR_UNSUPPORTED;
+  if (!kvq::f16k::attn_supported(cache->head_dim, cache->v_format)) return KVQ_ERR_UNSUPPORTED;
+  const kvq::SplitPlan plan = kvq::plan_splits(*cache, n_seq, n_qtok, n_q_heads, max_seq_len);
+  const size_t need = kvq::workspace_layout(*cache, n_seq, n_qtok, n_q_heads, plan).total;
+  if (workspace_bytes < need || !workspace) return KVQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KVQ_ERR_INVALID;
+  const int r = kvq::f16k::launch_attn(*cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs,
+                                       seq_len, plan, sm_scale, causal ? 1 : 0, workspace, nullptr,
+                                       nullptr, 0, static_cast<hipStream_t>(stream));
+  return r ? KVQ_ERR_HIP : KVQ_OK;
 }
 
 int kvq_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

@@ -33,6 +33,7 @@ struct AppendParams {
   int seg_tokens;
   int max_segs;
   int v_format;
+  int k_f16;         // 1: K rows stored as fp16 (the fp16-K A/B cache), no K scales
 };
 
 __global__ __launch_bounds__(256) void k_append_quant(AppendParams p) {
@@ -62,7 +63,9 @@ __global__ __launch_bounds__(256) void k_append_quant(AppendParams p) {
   const int t = (int)(prow - tile0);
 
   // ---- K
-  {
+  if (p.k_f16) {
+    reinterpret_cast<uint16_t*>(p.k_qs)[prow * p.head_dim + b * kBlock + e] = f32_to_half_bits(xk);
+  } else {
     int code;
     const uint16_t dbits = quant_sym8(xk, code);
     p.k_qs[prow * p.head_dim + b * kBlock + e] = (uint8_t)code;
@@ -85,7 +88,7 @@ __global__ __launch_bounds__(256) void k_append_quant(AppendParams p) {
 
 int launch_append(const kvq_cache& c, const float* k_new, const float* v_new, int n_seq, int n_new,
                   const int32_t* seg_table, int max_segs, const int32_t* start_pos,
-                  hipStream_t stream) {
+                  hipStream_t stream, bool k_f16) {
   AppendParams p;
   p.k_new = k_new;
   p.v_new = v_new;
@@ -102,6 +105,7 @@ int launch_append(const kvq_cache& c, const float* k_new, const float* v_new, in
   p.seg_tokens = c.seg_tokens;
   p.max_segs = max_segs;
   p.v_format = c.v_format;
+  p.k_f16 = k_f16 ? 1 : 0;
   const long long threads = (long long)p.n_units * kBlock;
   const int block = 256;
   const unsigned grid = (unsigned)((threads + block - 1) / block);

@@ -50,11 +50,24 @@
 
 #include <type_traits>
 
+// KVQ_KFMT selects the K format this file is compiled for: 0 is the packed
+// int8 K of the method; 1 is K kept as fp16 rows, the unpacked baseline page 1
+// compares against (A/B reference only, compiled from kvq_attn_f16k.hip into
+// namespace kvq::f16k, column layout and head_dim 128 only).  Its K tiles are
+// twice as large, so that build runs 6 waves with 2 ring slots each.
+#ifndef KVQ_KFMT
+#define KVQ_KFMT 0
+#endif
+
 namespace kvq {
+#if KVQ_KFMT == 1
+namespace f16k {
+#endif
 
 #ifndef KVQ_WAVES
 #define KVQ_WAVES 8
 #endif
+constexpr bool kF16K = KVQ_KFMT == 1;
 constexpr int kWaves = KVQ_WAVES;          // one work-group fills a CU
 constexpr int kThreads = kWaves * 64;
 constexpr int kLdsBudget = 163840 - 512;   // LDS of one work-group, less the small shared words
@@ -127,15 +140,16 @@ template <int D, int VF>
 struct Slot {
   static constexpr int NB = D / kBlock;
   static constexpr int VROW = VF == 0 ? D / 2 : D;   // V payload bytes per token
-  static constexpr int KBYTES = kTile * D;           // K codes of the tile
+  static constexpr int KROW = kF16K ? 2 * D : D;     // K bytes per token
+  static constexpr int KBYTES = kTile * KROW;        // K of the tile
   static constexpr int VBYTES = kTile * VROW;        // V payload of the tile
   static constexpr int SBYTES = kTile * NB * 2;      // one scale plane of the tile
   static constexpr int K_OFF = 0;
   static constexpr int V_OFF = KBYTES;
-  static constexpr int DK_OFF = KBYTES + VBYTES;
-  static constexpr int DV_OFF = DK_OFF + SBYTES;
+  static constexpr int DK_OFF = KBYTES + VBYTES;     // (fp16 K has no scale plane)
+  static constexpr int DV_OFF = DK_OFF + (kF16K ? 0 : SBYTES);
   static constexpr int BYTES = DV_OFF + SBYTES;
-  static constexpr int CPR = D / 16;                 // 16-byte chunks per K row
+  static constexpr int CPR = KROW / 16;              // 16-byte chunks per K row
   static constexpr int PBYTES = kRows * (kTile + 4) * 4;   // padded P staging tile (row layout)
   static constexpr bool P_IN_K = PBYTES <= KBYTES;   // P can reuse the K area
   static constexpr int PBUF = P_IN_K ? 0 : kWaves * PBYTES;   // row layout only
@@ -146,15 +160,20 @@ struct Slot {
   static constexpr int PATCH = kMaxAppend * PTOK;   // patch buffer, after the ring
   // three slots per wave where they fit in the CU's LDS, else two
   static constexpr int NSLOT = (3 * BYTES * kWaves + PBUF + PATCH <= kLdsBudget) ? 3 : 2;
-  static constexpr int QSTAGE = 1024;                // fp32 Q rows of one wave (at most 1 KB)
+  static constexpr int RPW = (kRows + kWaves - 1) / kWaves;   // Q rows per wave
+  static constexpr int QSTAGE = RPW * D * 4;         // fp32 Q rows of one wave
+  // Q operands shared through wave 0's last slot: int8 codes and fp32 block
+  // scales, or fp16 values for fp16 K
+  static constexpr int QOPS = kF16K ? kRows * D * 2 : kRows * D + kRows * NB * 4;
   // fp32 appended rows staged in a wave's last slot, behind the Q staging
-  // (and, in wave 0, the Q codes and scales)
-  static constexpr int STAGE = (QSTAGE + kRows * D + kRows * NB * 4 + 15) & ~15;
+  // (and, in wave 0, the Q operands)
+  static constexpr int STAGE = (QSTAGE + QOPS + 15) & ~15;
   static constexpr int STAGE_UNITS = (2 * kMaxAppend + kWaves - 1) / kWaves;   // rows per wave
-  static constexpr int LPT = KBYTES / 1024 + VBYTES / 1024 + (SBYTES == 256 ? 2 : 1);   // loads per tile
+  // loads per tile: K, V, and the scale planes (one load when they are 128 B)
+  static constexpr int LPT = KBYTES / 1024 + VBYTES / 1024 + (kF16K || SBYTES != 256 ? 1 : 2);
   static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "whole 1 KB load steps");
-  static_assert((kRows + kWaves - 1) / kWaves * D * 4 <= QSTAGE && QSTAGE + kRows * D + kRows * NB * 4 <= BYTES,
-                "Q staging does not fit a slot");
+  static_assert(!kF16K || SBYTES == 256, "fp16 K: the V scale plane is one 256-byte load");
+  static_assert(QSTAGE + QOPS <= BYTES, "Q staging does not fit a slot");
   static_assert(NSLOT * BYTES * kWaves + PBUF + PATCH <= kLdsBudget, "ring does not fit the LDS");
   static_assert(STAGE + STAGE_UNITS * D * 4 <= BYTES, "appended rows do not fit a slot");
 };
@@ -208,7 +227,8 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 // idle and doubled the cycles of every K read).
 template <int CPR>
 __device__ __forceinline__ int kswz(int t) {
-  if constexpr (CPR == 8) return (2 * ((t ^ (t >> 3)) & 3)) | ((t >> 2) & 1);
+  if constexpr (CPR == 16) return t & 15;   // fp16 K rows: chunk 4b + g read by 16 rows at once
+  else if constexpr (CPR == 8) return (2 * ((t ^ (t >> 3)) & 3)) | ((t >> 2) & 1);
   else return (t ^ (t >> 3)) & 3;
 }
 
@@ -228,11 +248,11 @@ __device__ __forceinline__ TileLane<D, VF> tile_lane_offsets(int lane) {
   const int r = lane / S::CPR;
   const int R = lane >> 1;
   const int c = (lane & 1) ^ ((R >> 2) & 1);
-  constexpr int ROWS_PER_KB = 1024 / D;
+  constexpr int ROWS_PER_KB = 1024 / S::KROW;
 #pragma unroll
   for (int n = 0; n < S::KBYTES / 1024; ++n) {
     const int q = (lane % S::CPR) ^ kswz<S::CPR>(r + ROWS_PER_KB * n);
-    t.k[n] = (uint32_t)(r * D + 16 * q + 1024 * n);
+    t.k[n] = (uint32_t)(r * S::KROW + 16 * q + 1024 * n);
   }
 #pragma unroll
   for (int n = 0; n < S::VBYTES / 1024; ++n) t.v[n] = (uint32_t)(R * 32 + 16 * c + 1024 * n);
@@ -264,7 +284,7 @@ __device__ __forceinline__ void issue_tile(const AttnParams& p, int seq, int kvh
     cur.base = ((long long)seg * p.n_kv_heads + kvh) * p.seg_tokens - lo;
   }
   const long long row0 = cur.base + t0;
-  const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.k_qs) + row0 * D;
+  const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.k_qs) + row0 * S::KROW;
 #pragma unroll
   for (int n = 0; n < S::KBYTES / 1024; ++n) dma<16>(kg, tl.k[n], slot + S::K_OFF + 1024 * n);
   const uint8_t* vg = p.v_qs + row0 * S::VROW;
@@ -272,7 +292,9 @@ __device__ __forceinline__ void issue_tile(const AttnParams& p, int seq, int kvh
   for (int n = 0; n < S::VBYTES / 1024; ++n) dma<16>(vg, tl.v[n], slot + S::V_OFF + 1024 * n);
   const uint8_t* kdg = reinterpret_cast<const uint8_t*>(p.k_d) + row0 * S::NB * 2;
   const uint8_t* vdg = reinterpret_cast<const uint8_t*>(p.v_d) + row0 * S::NB * 2;
-  if constexpr (S::SBYTES == 256) {
+  if constexpr (kF16K) {
+    dma<4>(vdg, tl.s, slot + S::DV_OFF);
+  } else if constexpr (S::SBYTES == 256) {
     dma<4>(kdg, tl.s, slot + S::DK_OFF);
     dma<4>(vdg, tl.s, slot + S::DV_OFF);
   } else {
@@ -517,21 +539,24 @@ __device__ __forceinline__ void prologue(const AttnParams& p, uint8_t* s_lds, in
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
   constexpr int NSLOT = S::NSLOT;
-  constexpr int RPW = (kRows + kWaves - 1) / kWaves;   // Q rows per wave
+  constexpr int RPW = S::RPW;            // Q rows per wave
   constexpr int PIECES = RPW * D / 4;   // 16-byte pieces of them
-  static_assert(PIECES <= 64, "one load per wave");
   const int lane = __lane_id();
   const int R = p.rows, G = p.group;
   uint8_t* ring = s_lds + wave * NSLOT * S::BYTES;
   const uint32_t ring_lds = lds_addr(ring);
-  {
-    // lanes past PIECES repeat the first pieces into the unused half
-    const int pc = lane % PIECES;
-    const int r = wave + kWaves * (pc / (D / 4));
-    const int rr = r < R ? r : 0;
-    const float* src = p.q + (((size_t)seq * p.n_qtok + rr / G) * p.n_q_heads + kvh * G + rr % G) * D +
-                       4 * (pc % (D / 4));
-    dma16_v(src, ring_lds + (NSLOT - 1) * S::BYTES);
+#pragma unroll
+  for (int base = 0; base < PIECES; base += 64) {
+    // one piece per lane; lanes past PIECES stay idle (their bytes would
+    // land on the Q operands other waves write into wave 0's slot)
+    const int pc = base + lane;
+    if (base + 64 <= PIECES || pc < PIECES) {
+      const int r = wave + kWaves * (pc / (D / 4));
+      const int rr = r < R ? r : 0;
+      const float* src = p.q + (((size_t)seq * p.n_qtok + rr / G) * p.n_q_heads + kvh * G + rr % G) * D +
+                         4 * (pc % (D / 4));
+      dma16_v(src, ring_lds + (NSLOT - 1) * S::BYTES + 16 * base);
+    }
   }
   // appended rows, ahead of the tiles so that waiting for them leaves the
   // tiles in flight
@@ -554,8 +579,15 @@ __device__ __forceinline__ void prologue(const AttnParams& p, uint8_t* s_lds, in
   for (int k = 0; k < RPW; ++k) {
     const int r = wave + kWaves * k;
     if (r >= kRows) break;
+    if constexpr (kF16K) {
+      // fp16 K: Q enters the f16 dot as fp16 values
+      _Float16* s_qh = reinterpret_cast<_Float16*>(s_qc);
 #pragma unroll
-    for (int e = 0; e < D / 64; ++e) quantize_q_lane(qv[k][e], 64 * e + lane, s_qc + r * D, s_qd + r * NB);
+      for (int e = 0; e < D / 64; ++e) s_qh[r * D + 64 * e + lane] = (_Float16)qv[k][e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < D / 64; ++e) quantize_q_lane(qv[k][e], 64 * e + lane, s_qc + r * D, s_qd + r * NB);
+    }
   }
   if (app.hi > app.lo)
     quantize_appended<D, VF>(app, wave, reinterpret_cast<const float*>(ring + (NSLOT - 1) * S::BYTES + S::STAGE),
@@ -609,7 +641,8 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, 
   constexpr int kBatch = 16;                              // partial loads in flight per thread
   static_assert(kMaxSplits * kRows * 4 + 16 * kThreads <= LDS_BYTES,
                 "split merge does not fit the LDS buffer");
-  static_assert(kRows * D / 4 <= kThreads, "one thread per output column at least");
+  // (the fp16-K build runs the column layout only: at most 4 rows)
+  static_assert(kF16K || kRows * D / 4 <= kThreads, "one thread per output column at least");
   const int tid = threadIdx.x;
   const int R = p.rows, G = p.group;
   float* s_m = s_buf + kWaves * kRows * D;
@@ -1042,10 +1075,14 @@ __device__ __forceinline__ float sum_blocks(float x) {
   return x;
 }
 
+// The Q operand of one block for this lane: 8 int8 codes, or 8 fp16 values
+// for fp16 K.
+using QOp = std::conditional_t<kF16K, v8h, long>;
+
 template <int D, int VF>
 __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, int c1, bool full,
                                                   bool first, int vis, bool valid,
-                                                  const long (&qb)[D / kBlock], float wq,
+                                                  const QOp (&qb)[D / kBlock], float wq,
                                                   ColState<D>& st) {
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
@@ -1057,28 +1094,46 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
   // ---- int32 block dots.  Half h feeds row m of A with the K row of token
   // 8*(m/4) + 4h + m%4, so output row 4*grp + i of half h is token
   // 8*grp + 4h + i: this lane ends up with tokens 8*grp .. +8 in order.
-  v4i cq[2];
+  float s[8];   // scores minus the running maximum, log2 domain, tokens t0 + 8*grp + j
+  if constexpr (kF16K) {
+    // fp16 K: the block dots come out of the f16 MFMA in fp32, and only the
+    // softmax scale (wq) applies
+    v4f cf[2];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    cq[h] = (v4i){0, 0, 0, 0};
-    const int tau = 8 * (col >> 2) + 4 * h + (col & 3);
+    for (int h = 0; h < 2; ++h) {
+      cf[h] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
+      const int tau = 8 * (col >> 2) + 4 * h + (col & 3);
 #pragma unroll
-    for (int bb = 0; bb < NB; ++bb) {
-      const int q = 2 * bb + (grp >> 1);
-      const long ka = *reinterpret_cast<const long*>(
-          slot + S::K_OFF + (tau * S::CPR + (q ^ kswz<S::CPR>(tau))) * 16 + 8 * (grp & 1));
-      cq[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ka, qb[bb], cq[h], 0, 0, 0);
+      for (int bb = 0; bb < NB; ++bb) {
+        const int q = 4 * bb + grp;   // dims 32bb + 8grp .. +8
+        const v8h ka = *reinterpret_cast<const v8h*>(slot + S::K_OFF +
+                                                     (tau * S::CPR + (q ^ kswz<S::CPR>(tau))) * 16);
+        cf[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[bb], cf[h], 0, 0, 0);
+      }
     }
-  }
-
-  // ---- scores minus the running maximum, log2 domain, tokens t0 + 8*grp + j
-  const uint4 dkw = *reinterpret_cast<const uint4*>(slot + S::DK_OFF + b * 64 + 16 * grp);
-  const uint32_t dkv[4] = {dkw.x, dkw.y, dkw.z, dkw.w};
-  float s[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float w = (j & 1) ? mul_f32_f16<1>(wq, dkv[j >> 1]) : mul_f32_f16<0>(wq, dkv[j >> 1]);
-    s[j] = fmaf((float)cq[j >> 2][j & 3], w, st.c0);
+    for (int j = 0; j < 8; ++j) s[j] = fmaf(cf[j >> 2][j & 3], wq, st.c0);
+  } else {
+    v4i cq[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      cq[h] = (v4i){0, 0, 0, 0};
+      const int tau = 8 * (col >> 2) + 4 * h + (col & 3);
+#pragma unroll
+      for (int bb = 0; bb < NB; ++bb) {
+        const int q = 2 * bb + (grp >> 1);
+        const long ka = *reinterpret_cast<const long*>(
+            slot + S::K_OFF + (tau * S::CPR + (q ^ kswz<S::CPR>(tau))) * 16 + 8 * (grp & 1));
+        cq[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ka, qb[bb], cq[h], 0, 0, 0);
+      }
+    }
+    const uint4 dkw = *reinterpret_cast<const uint4*>(slot + S::DK_OFF + b * 64 + 16 * grp);
+    const uint32_t dkv[4] = {dkw.x, dkw.y, dkw.z, dkw.w};
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float w = (j & 1) ? mul_f32_f16<1>(wq, dkv[j >> 1]) : mul_f32_f16<0>(wq, dkv[j >> 1]);
+      s[j] = fmaf((float)cq[j >> 2][j & 3], w, st.c0);
+    }
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) s[j] = sum_blocks<NB>(s[j]);
@@ -1204,11 +1259,20 @@ __global__ __launch_bounds__(kThreads) void k_attn_cols(AttnParams p) {
   // the columns of block bb only
   const int r = col / NB, b = col % NB;
   const bool valid = r < R;
-  long qb[NB];
+  QOp qb[NB];
 #pragma unroll
-  for (int bb = 0; bb < NB; ++bb)
-    qb[bb] = (valid && bb == b) ? *reinterpret_cast<const long*>(s_qc + r * D + kBlock * bb + 8 * grp) : 0;
-  const float wq = valid ? s_qd[r * NB + b] * p.scale_log2 : 0.0f;
+  for (int bb = 0; bb < NB; ++bb) {
+    if constexpr (kF16K) {
+      const _Float16* s_qh = reinterpret_cast<const _Float16*>(s_qc);
+      qb[bb] = (valid && bb == b) ? *reinterpret_cast<const v8h*>(s_qh + r * D + kBlock * bb + 8 * grp)
+                                  : (v8h){};
+    } else {
+      qb[bb] = (valid && bb == b) ? *reinterpret_cast<const long*>(s_qc + r * D + kBlock * bb + 8 * grp) : 0;
+    }
+  }
+  float wq;
+  if constexpr (kF16K) wq = valid ? p.scale_log2 : 0.0f;
+  else wq = valid ? s_qd[r * NB + b] * p.scale_log2 : 0.0f;
   const int vis = valid ? min(p.causal ? L - p.n_qtok + r / G + 1 : L, c1) : 0;
   const int vis_min = min(p.causal ? L - p.n_qtok + 1 : L, c1);   // the first query token's
   __syncthreads();   // every wave has its operands; wave 0's last slot is free
@@ -1313,12 +1377,16 @@ __global__ __launch_bounds__(64) void k_split_merge(AttnParams p) {
 }
 
 bool attn_supported(int head_dim, int v_format) {
-  return (head_dim == 64 || head_dim == 128) && (v_format == 0 || v_format == 1);
+  return (head_dim == 128 || (!kF16K && head_dim == 64)) && (v_format == 0 || v_format == 1);
 }
 
 template <int D, int VF>
 static void launch_attn_kernel(AttnParams p, dim3 grid, hipStream_t stream) {
-  if (p.rows * (D / kBlock) <= 16) {
+  if constexpr (kF16K) {
+    // column layout only (the caller checks rows * blocks <= 16)
+    p.merge_launch = 0;
+    hipLaunchKernelGGL((k_attn_cols<D, VF>), grid, dim3(kThreads), 0, stream, p);
+  } else if (p.rows * (D / kBlock) <= 16) {
     p.merge_launch = 0;
     hipLaunchKernelGGL((k_attn_cols<D, VF>), grid, dim3(kThreads), 0, stream, p);
   } else {
@@ -1371,13 +1439,18 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
       launch_attn_kernel<128, 0>(p, grid, stream);
     else
       launch_attn_kernel<128, 1>(p, grid, stream);
-  } else {
+  } else if constexpr (!kF16K) {
     if (c.v_format == 0)
       launch_attn_kernel<64, 0>(p, grid, stream);
     else
       launch_attn_kernel<64, 1>(p, grid, stream);
+  } else {
+    return -4;   // not reached: the entry point checks head_dim
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
+#if KVQ_KFMT == 1
+}  // namespace f16k
+#endif
 }  // namespace kvq

@@ -33,9 +33,10 @@ SplitPlan plan_splits(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads, 
 WorkspaceLayout workspace_layout(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads,
                                  const SplitPlan& plan);
 
+// k_f16: the cache's k_qs holds fp16 K rows (the fp16-K A/B cache) and k_d is unused.
 int launch_append(const kvq_cache& c, const float* k_new, const float* v_new, int n_seq, int n_new,
                   const int32_t* seg_table, int max_segs, const int32_t* start_pos,
-                  hipStream_t stream);
+                  hipStream_t stream, bool k_f16 = false);
 
 bool attn_supported(int head_dim, int v_format);
 
@@ -46,6 +47,16 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
                 const int32_t* seg_table, int max_segs, const int32_t* seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
                 const float* k_new, const float* v_new, int n_new, hipStream_t stream);
+
+// The same attention kernels compiled for fp16 K rows (kvq_attn_f16k.hip):
+// head_dim 128, column layout (query rows x 4 blocks <= 16), no append.
+namespace f16k {
+bool attn_supported(int head_dim, int v_format);
+int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
+                const int32_t* seg_table, int max_segs, const int32_t* seq_len,
+                const SplitPlan& plan, float sm_scale, int causal, void* workspace,
+                const float* k_new, const float* v_new, int n_new, hipStream_t stream);
+}  // namespace f16k
 
 int launch_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);
 int launch_debug_quant_q(const float* q, int n_rows, int head_dim, int8_t* codes, float* scales,

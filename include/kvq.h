@@ -197,6 +197,35 @@ int attn_decode_packed_append(const kvq_cache* cache, const float* q, const floa
 int kvq_debug_quant_q(const float* q, int n_rows, int head_dim, int8_t* codes, float* scales,
                       void* stream);
 /*
+ * fp16-K reference for A/B measurements (not the method).  Page 1 compares
+ * its packed int8 K with K kept as fp16; these calls run the same attention
+ * kernels on a cache whose K is plain fp16 rows, so both can be timed on the
+ * same hardware and the time compared with the bytes each moves.
+ *
+ * The cache is a kvq_cache with head_dim 128 whose k_qs points to binary16 K
+ * rows [seg][kv_head][token][128] (256 bytes per token) and whose k_d is
+ * NULL; V is stored exactly as in the packed cache.  kvq_f16k_cache_bytes
+ * gives the plane sizes (out_bytes[1] = 0).  kv_append_f16k writes K as
+ * fp16 (round to nearest even) and V as kv_append_quant does.
+ * attn_decode_f16k computes softmax(sm_scale * q16 . k16) v over the cache,
+ * with q16 = q rounded to binary16 and the dot in fp32; it takes the column
+ * layout's shapes only (n_qtok * n_q_heads / n_kv_heads <= 4, else
+ * KVQ_ERR_UNSUPPORTED) and no appended rows.  Arguments, workspace and
+ * errors otherwise as attn_decode_packed.
+ */
+int kvq_f16k_cache_bytes(int n_kv_heads, int head_dim, int seg_tokens, int n_segs, int v_format,
+                         size_t out_bytes[4]);
+int kv_append_f16k(const kvq_cache* cache, const float* k_new, const float* v_new, int n_seq,
+                   int n_new, const int32_t* seg_table, int max_segs, const int32_t* start_pos,
+                   void* stream);
+int attn_decode_f16k_workspace_size(const kvq_cache* cache, int n_seq, int n_qtok, int n_q_heads,
+                                    int max_seq_len, size_t* bytes);
+int attn_decode_f16k(const kvq_cache* cache, const float* q, float* out, int n_seq, int n_qtok,
+                     int n_q_heads, const int32_t* seg_table, int max_segs, const int32_t* seq_len,
+                     int max_seq_len, float sm_scale, int causal, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * kvq_debug_stream_read: measurement hook, not part of the method.  Reads
  * `bytes` (a nonzero multiple of 16) of device memory at `buf` (16-byte
  * aligned) with plain 16-byte loads and discards them; `sink` (device, one

@@ -290,6 +290,35 @@ def decode_attention(q, k_words, k_d, v_payload, v_d, v_format: int, seq_len,
     return out
 
 
+def decode_attention_f16k(q, k_bits, v_payload, v_d, v_format: int, seq_len, sm_scale: float,
+                          causal: bool, q_heads=None) -> np.ndarray:
+    """Attention of the fp16-K reference that page 1 compares its packed K
+    against (an A/B reference, not the method): K kept as binary16 rows, Q
+    rounded to binary16, the dot of the two exact fp16 values, V dequantized
+    as in decode_attention.
+
+    k_bits    uint16 [S][Hkv][Lmax][D]  binary16 bit patterns
+    other arguments and the result as decode_attention."""
+    q = np.asarray(q, dtype=F32)
+    S, Tq, Hq, D = q.shape
+    Hkv = k_bits.shape[1]
+    G = Hq // Hkv
+    heads = range(Hq) if q_heads is None else q_heads
+    out = np.full((S, Tq, Hq, D), np.nan)
+    q_hat = half_value(half_bits(q)).astype(np.float64)
+    for i in range(S):
+        L = int(seq_len[i])
+        vis = visible_tokens(L, Tq, causal)
+        for kvh in sorted({h // G for h in heads}):
+            k_hat = half_value(k_bits[i, kvh, :L]).astype(np.float64)
+            v_hat = dequant_v(v_payload[i, kvh, :L], v_d[i, kvh, :L], v_format)
+            for h in heads:
+                if h // G != kvh:
+                    continue
+                out[i, :, h, :] = softmax_attention(q_hat[i, :, h, :], k_hat, v_hat, sm_scale, vis)
+    return out
+
+
 def kv_bytes_per_token_head(head_dim: int, v_format: int):
     """(K bytes, V bytes) one token of one kv head occupies: payload plus one
     fp16 scale per 32-block."""

@@ -134,3 +134,27 @@ def test_bad_fused_append_args_rejected():
     assert call(n_new=4, max_len=2) == K.KVQ_ERR_INVALID      # more new rows than tokens
     assert call(hq=12) == K.KVQ_ERR_INVALID                   # the attention checks still apply
     assert call(ws_bytes=16) == K.KVQ_ERR_WORKSPACE
+
+
+def test_f16k_reference_args_rejected():
+    """The fp16-K A/B entry points: K rows without a scale plane (k_d NULL),
+    head_dim 128 only, column-layout shapes only; validation before launch."""
+    L = K.lib()
+    c = _fake_cache(k_d=None)
+
+    def attn(cache=c, n_qtok=1, hq=32, ws_bytes=1 << 30):
+        return L.attn_decode_f16k(ctypes.byref(cache), 0x5000, 0x6000, 1, n_qtok, hq, None, 1, 0x7000,
+                                  1024, 0.1, 0, 0x8000, ws_bytes, None)
+
+    assert attn(cache=_fake_cache()) == K.KVQ_ERR_INVALID              # a packed cache (k_d set)
+    assert attn(cache=_fake_cache(k_d=None, head_dim=64)) == K.KVQ_ERR_UNSUPPORTED
+    assert attn(n_qtok=2) == K.KVQ_ERR_UNSUPPORTED                      # 8 rows x 4 blocks > 16
+    assert attn(ws_bytes=16) == K.KVQ_ERR_WORKSPACE
+    assert L.kv_append_f16k(ctypes.byref(_fake_cache()), 0x9000, 0xA000, 1, 1, None, 1, 0x7000,
+                            None) == K.KVQ_ERR_INVALID
+    out = (ctypes.c_size_t * 4)()
+    assert L.kvq_f16k_cache_bytes(8, 128, 1024, 2, 0, out) == K.KVQ_OK
+    assert tuple(out) == (2 * 8 * 1024 * 256, 0, 2 * 8 * 1024 * 64, 2 * 8 * 1024 * 8)
+    n = ctypes.c_size_t(0)
+    assert L.attn_decode_f16k_workspace_size(ctypes.byref(c), 1, 1, 32, 1024, ctypes.byref(n)) == K.KVQ_OK
+    assert n.value > 0

@@ -188,3 +188,39 @@ def test_visible_tokens():
     assert list(O.visible_tokens(10, 1, True)) == [10]
     assert list(O.visible_tokens(10, 4, True)) == [7, 8, 9, 10]
     assert list(O.visible_tokens(10, 4, False)) == [10, 10, 10, 10]
+
+
+def test_f16k_reference_on_representable_inputs():
+    """decode_attention_f16k rounds Q and K to binary16; on inputs that
+    binary16 holds exactly the rounding is the identity, so the result is the
+    (mpmath-pinned) softmax attention of the raw values.  K values are
+    multiples of 1/64 in [-4, 4] and Q multiples of 1/256 in [-2, 2]."""
+    rng = np.random.default_rng(41)
+    S, Tq, Hq, Hkv, D, L = 1, 1, 4, 2, 128, 96
+    q = (rng.integers(-512, 513, (S, Tq, Hq, D)) / 256.0).astype(np.float32)
+    k = (rng.integers(-256, 257, (S, Hkv, L, D)) / 64.0).astype(np.float32)
+    v = rng.standard_normal((S, Hkv, L, D)).astype(np.float32)
+    k_bits = O.half_bits(k)
+    assert np.array_equal(O.half_value(k_bits), k)
+    vp, vd = O.encode_v(v, O.V_Q4_0)
+    got = O.decode_attention_f16k(q, k_bits, vp, vd, O.V_Q4_0, [L], D ** -0.5, False)
+    for h in range(Hq):
+        kvh = h // (Hq // Hkv)
+        want = O.softmax_attention(q[0, :, h].astype(np.float64), k[0, kvh].astype(np.float64),
+                                   O.dequant_v(vp[0, kvh], vd[0, kvh], O.V_Q4_0), D ** -0.5, [L])
+        np.testing.assert_array_equal(got[0, :, h], want)
+
+
+def test_f16k_reference_rounds_inputs():
+    """Away from representable values the reference sees the rounded inputs:
+    it equals the exact attention of half_value(half_bits(x))."""
+    rng = np.random.default_rng(42)
+    q = rng.standard_normal((1, 1, 2, 128)).astype(np.float32)
+    k = rng.standard_normal((1, 1, 64, 128)).astype(np.float32)
+    v = rng.standard_normal((1, 1, 64, 128)).astype(np.float32)
+    vp, vd = O.encode_v(v, O.V_Q8_0)
+    got = O.decode_attention_f16k(q, O.half_bits(k), vp, vd, O.V_Q8_0, [64], 0.1, False)
+    raw = O.decode_attention_f16k(O.half_value(O.half_bits(q)), O.half_bits(k), vp, vd, O.V_Q8_0,
+                                  [64], 0.1, False)
+    np.testing.assert_array_equal(got, raw)   # rounding twice changes nothing
+    assert np.abs(O.half_value(O.half_bits(q)) - q).max() > 0
