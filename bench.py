@@ -257,6 +257,54 @@ def other_configs(K, W, torch, stream, steps: int, warmup: int) -> list:
     return rows
 
 
+def ab_f16k(K, torch, stream, ci, caches, steps: int, warmup: int) -> dict:
+    """Page 1's comparison on this hardware: attention alone over the same
+    long128k inputs with the packed int8 K (the method) and with K kept as
+    fp16 rows (attn_decode_f16k), both with q4_0 V and rotating replicas.  If
+    the time follows the bytes, the time ratio equals the byte ratio."""
+    spec = ci.spec
+    L = spec.ctx
+    f16 = []
+    for _ in range(len(caches)):
+        c = K.F16KCache(spec.n_kv_heads, spec.head_dim, ci.seg_tokens, 1, spec.v_format)
+        K.kv_append_f16k(c, torch.from_numpy(ci.k).cuda(), torch.from_numpy(ci.v).cuda(),
+                         torch.zeros(1, dtype=torch.int32, device="cuda"))
+        f16.append(c)
+    torch.cuda.synchronize()
+    q = torch.from_numpy(ci.q).cuda()
+    out = torch.empty_like(q)
+    sl = torch.tensor([L], dtype=torch.int32, device="cuda")
+    ws = torch.zeros(max(K.attn_decode_packed_workspace_size(caches[0], 1, 1, spec.n_q_heads, L),
+                         K.attn_decode_f16k_workspace_size(f16[0], 1, 1, spec.n_q_heads, L)),
+                     dtype=torch.uint8, device="cuda")
+    runs = {"packed_int8_k": (caches, K.attn_decode_packed), "fp16_k": (f16, K.attn_decode_f16k)}
+    res = {}
+    for name, (cs, fn) in runs.items():
+        for i in range(warmup):
+            fn(cs[i % len(cs)], q, out, sl, L, spec.sm_scale, False, ws, stream=stream)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            fn(cs[i % len(cs)], q, out, sl, L, spec.sm_scale, False, ws, stream=stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / steps
+        per = (2 * spec.head_dim if name == "fp16_k" else algorithmic_bytes(spec, 1, 0)["per_token_head"]
+               - (spec.head_dim // 2 + 2 * (spec.head_dim // 32)))
+        kvb = L * spec.n_kv_heads * (per + spec.head_dim // 2 + 2 * (spec.head_dim // 32))
+        res[name] = {"us": round(us, 2), "kv_bytes": kvb, "gbs": round(kvb / us / 1e3, 1),
+                     "pct_hbm_peak": round(100 * kvb / us / 1e3 / HBM_PEAK_GBS, 1)}
+    res["byte_ratio"] = round(res["fp16_k"]["kv_bytes"] / res["packed_int8_k"]["kv_bytes"], 3)
+    res["time_ratio"] = round(res["fp16_k"]["us"] / res["packed_int8_k"]["us"], 3)
+    res["note"] = ("attention only; fp16 K: 6 waves x 2 ring slots (its 8 KB K tiles), "
+                   "Q rounded to fp16, f16 MFMA for Q.K")
+    print(f"[bench] A/B fp16 K: {res['fp16_k']['us']} us vs packed {res['packed_int8_k']['us']} us "
+          f"(time x{res['time_ratio']}, bytes x{res['byte_ratio']})", file=sys.stderr, flush=True)
+    del f16
+    return res
+
+
 def cpu_baseline(ci, target_s: float = 12.0) -> dict:
     """The oracle on the host: the same step (quantize the new token into
     the packed cache, then attention over all tokens from the packed cache),
@@ -489,6 +537,8 @@ def main() -> int:
     print(f"[bench] timed: {ms_step * 1e3:.2f} us/step, attention {attn_ms.mean() * 1e3:.2f} us",
           file=sys.stderr, flush=True)
     if not args.no_other_configs:
+        result["ab_f16k"] = ab_f16k(K, torch, stream, ci, caches, max(100, args.steps // 4),
+                                    max(20, args.warmup // 4))
         del caches
         torch.cuda.empty_cache()
         result["other_configs"] = other_configs(K, W, torch, stream, max(50, args.steps // 5),
