@@ -252,6 +252,30 @@ def other_configs(K, W, torch, stream, steps: int, warmup: int) -> list:
                      "gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                      "launches_per_step": len(names), "replicas": reps})
         print(f"[bench] {label}: {ms * 1e3:.2f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
+        if len(calls) > 1:
+            # the same calls as one attn_decode_packed_batch launch
+            def batch_args(i):
+                return [dict(cache=built[i % len(built)][0], q=q, out=out, seq_len=sl, max_seq_len=mx,
+                             sm_scale=spec.sm_scale, causal=spec.causal, seg_table=built[i % len(built)][1])
+                        for built, q, out, sl, mx, spec, _ in calls]
+            bws = torch.zeros(K.attn_decode_packed_batch_workspace_size(batch_args(0)), dtype=torch.uint8,
+                              device="cuda")
+            args_r = [batch_args(i) for i in range(reps)]
+            for i in range(warmup):
+                K.attn_decode_packed_batch(args_r[i % reps], bws, stream=stream)
+            e0.record(stream)
+            for i in range(steps):
+                K.attn_decode_packed_batch(args_r[i % reps], bws, stream=stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            gbs = nbytes / (ms * 1e-3) / 1e9
+            rows.append({"workload": label + " (one batched launch)", "us_per_step": round(ms * 1e3, 2),
+                         "kv_bytes_per_step": nbytes, "gbs": round(gbs, 1),
+                         "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "launches_per_step": 1,
+                         "replicas": reps})
+            print(f"[bench] {label} batched: {ms * 1e3:.2f} us/step, {gbs:.0f} GB/s", file=sys.stderr,
+                  flush=True)
         del calls
         torch.cuda.empty_cache()
     return rows

@@ -10,6 +10,7 @@ from ._lib import (EXPORTS, KVQ_BLOCK, KVQ_ERR_HIP, KVQ_ERR_INVALID, KVQ_ERR_UNS
                    KvqCacheStruct, KvqError, PackedKVCache, attn_decode_packed,
                    attn_decode_packed_append, KVQ_MAX_APPEND, F16KCache, attn_decode_f16k,
                    attn_decode_f16k_workspace_size, kv_append_f16k, kvq_f16k_cache_bytes,
+                   attn_decode_packed_batch, attn_decode_packed_batch_workspace_size, KVQ_MAX_BATCH,
                    attn_decode_packed_workspace_size, kv_append_quant, kvq_abi_version,
                    kvq_cache_bytes, kvq_debug_qk_isum, kvq_debug_quant_q, kvq_debug_stream_read, lib,
                    status_string)
@@ -19,6 +20,7 @@ __all__ = ["EXPORTS", "KVQ_BLOCK", "KVQ_ERR_HIP", "KVQ_ERR_INVALID", "KVQ_ERR_UN
            "KVQ_V_Q8_0", "KvqCacheStruct", "KvqError", "PackedKVCache", "attn_decode_packed",
            "attn_decode_packed_append", "KVQ_MAX_APPEND", "F16KCache", "attn_decode_f16k",
            "attn_decode_f16k_workspace_size", "kv_append_f16k", "kvq_f16k_cache_bytes",
+           "attn_decode_packed_batch", "attn_decode_packed_batch_workspace_size", "KVQ_MAX_BATCH",
            "attn_decode_packed_workspace_size", "kv_append_quant", "kvq_abi_version",
            "kvq_cache_bytes", "kvq_debug_qk_isum", "kvq_debug_quant_q", "kvq_debug_stream_read", "lib",
            "status_string"]

@@ -25,18 +25,27 @@ KVQ_BLOCK = 32
 KVQ_SEG_ALIGN = 64
 KVQ_MAX_QTOK = 16
 KVQ_MAX_APPEND = 16
+KVQ_MAX_BATCH = 4
 
 EXPORTS = ("kvq_abi_version", "kvq_status_string", "kvq_cache_bytes", "kv_append_quant",
            "attn_decode_packed_append",
            "attn_decode_packed_workspace_size", "attn_decode_packed", "kvq_debug_quant_q",
            "kvq_debug_qk_isum", "kvq_debug_stream_read", "kvq_f16k_cache_bytes", "kv_append_f16k",
-           "attn_decode_f16k_workspace_size", "attn_decode_f16k")
+           "attn_decode_f16k_workspace_size", "attn_decode_f16k", "attn_decode_packed_batch",
+           "attn_decode_packed_batch_workspace_size")
 
 
 class KvqCacheStruct(ctypes.Structure):
     _fields_ = [("n_kv_heads", c_int32), ("head_dim", c_int32), ("seg_tokens", c_int32),
                 ("n_segs", c_int32), ("v_format", c_int32), ("reserved", c_int32),
                 ("k_qs", c_void_p), ("k_d", c_void_p), ("v_qs", c_void_p), ("v_d", c_void_p)]
+
+
+class KvqAttnCallStruct(ctypes.Structure):
+    _fields_ = [("cache", POINTER(KvqCacheStruct)), ("q", c_void_p), ("out", c_void_p),
+                ("n_seq", c_int32), ("n_qtok", c_int32), ("n_q_heads", c_int32),
+                ("seg_table", c_void_p), ("max_segs", c_int32), ("seq_len", c_void_p),
+                ("max_seq_len", c_int32), ("sm_scale", c_float), ("causal", c_int32)]
 
 
 class KvqError(RuntimeError):
@@ -85,6 +94,12 @@ def lib() -> ctypes.CDLL:
         L.attn_decode_f16k_workspace_size.argtypes = L.attn_decode_packed_workspace_size.argtypes
         L.attn_decode_f16k.restype = c_int
         L.attn_decode_f16k.argtypes = L.attn_decode_packed.argtypes
+        L.attn_decode_packed_batch_workspace_size.restype = c_int
+        L.attn_decode_packed_batch_workspace_size.argtypes = [POINTER(KvqAttnCallStruct), c_int,
+                                                              POINTER(c_size_t)]
+        L.attn_decode_packed_batch.restype = c_int
+        L.attn_decode_packed_batch.argtypes = [POINTER(KvqAttnCallStruct), c_int, c_void_p, c_size_t,
+                                               c_void_p]
         L.kvq_debug_stream_read.restype = c_int
         L.kvq_debug_stream_read.argtypes = [c_void_p, ctypes.c_size_t, c_void_p, c_void_p]
         L.kvq_debug_quant_q.restype = c_int
@@ -330,6 +345,49 @@ def attn_decode_packed_append(cache: PackedKVCache, q, k_new, v_new, out, seq_le
                                            int(max_seq_len), float(sm_scale), int(bool(causal)),
                                            _ptr(workspace), ws_bytes, _stream(stream)),
            "attn_decode_packed_append")
+
+
+def _batch_calls(calls):
+    """calls: dicts with cache, q, out, seq_len, max_seq_len, sm_scale, causal
+    and optionally seg_table / max_segs, as attn_decode_packed takes them."""
+    import torch
+    arr = (KvqAttnCallStruct * len(calls))()
+    for i, c in enumerate(calls):
+        cache, q, out, seq_len = c["cache"], c["q"], c["out"], c["seq_len"]
+        _need(q, torch.float32, "q", 4)
+        _need(out, torch.float32, "out", 4)
+        _need(seq_len, torch.int32, "seq_len", 1)
+        if q.shape != out.shape:
+            raise ValueError("q and out differ in shape")
+        n_seq, n_qtok, n_q_heads, d = q.shape
+        if d != cache.head_dim or seq_len.shape[0] != n_seq:
+            raise ValueError("shape does not match the cache")
+        seg_table = c.get("seg_table")
+        if seg_table is not None:
+            _need(seg_table, torch.int32, "seg_table", 2)
+            max_segs = seg_table.shape[1]
+        else:
+            max_segs = c.get("max_segs") or cache.n_segs // n_seq
+        arr[i] = KvqAttnCallStruct(ctypes.pointer(cache.struct), _ptr(q), _ptr(out), n_seq, n_qtok,
+                                   n_q_heads, _ptr(seg_table), int(max_segs), _ptr(seq_len),
+                                   int(c["max_seq_len"]), float(c["sm_scale"]), int(bool(c["causal"])))
+    return arr
+
+
+def attn_decode_packed_batch_workspace_size(calls) -> int:
+    arr = _batch_calls(calls)
+    out = c_size_t(0)
+    _check(lib().attn_decode_packed_batch_workspace_size(arr, len(calls), ctypes.byref(out)),
+           "attn_decode_packed_batch_workspace_size")
+    return int(out.value)
+
+
+def attn_decode_packed_batch(calls, workspace, stream=None) -> None:
+    """Several attn_decode_packed calls (see _batch_calls) in one launch."""
+    arr = _batch_calls(calls)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().attn_decode_packed_batch(arr, len(calls), _ptr(workspace), ws_bytes, _stream(stream)),
+           "attn_decode_packed_batch")
 
 
 def kvq_debug_stream_read(buf, sink, stream=None) -> None:

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -195,7 +196,90 @@ int attn_common(const kvq_cache* cache, const float* q, float* out, int n_seq, i
   return r ? KVQ_ERR_HIP : KVQ_OK;
 }
 
+// Validate one call of a batch and convert it.
+int check_call(const kvq_attn_call* a, kvq::AttnCall* out) {
+  if (!a) return KVQ_ERR_INVALID;
+  int st = check_attn(a->cache, a->q, a->out, a->n_seq, a->n_qtok, a->n_q_heads, a->seg_table,
+                      a->max_segs, a->seq_len, a->max_seq_len);
+  if (st) return st;
+  if (!std::isfinite(a->sm_scale)) return KVQ_ERR_INVALID;
+  if (a->n_qtok * (a->n_q_heads / a->cache->n_kv_heads) > KVQ_MAX_QTOK) return KVQ_ERR_UNSUPPORTED;
+  if (!kvq::attn_supported(a->cache->head_dim, a->cache->v_format)) return KVQ_ERR_UNSUPPORTED;
+  *out = {a->cache, a->q, a->out, a->n_seq, a->n_qtok, a->n_q_heads, a->seg_table, a->max_segs,
+          a->seq_len, a->max_seq_len, a->sm_scale, a->causal ? 1 : 0};
+  return KVQ_OK;
+}
+
+// Validate a batch; on success fills calls[], plans[] and the workspace size.
+// One launch runs every call, so the split plan is joint: with fewer than
+// 256 (sequence, kv head) groups in all, one chunk length for every call,
+// the shortest multiple of 256 tokens that keeps the whole grid within one
+// work-group per CU; otherwise each call's own plan.
+int check_batch(const kvq_attn_call* calls, int n_calls, kvq::AttnCall* out, kvq::SplitPlan* plans,
+                size_t* ws_bytes) {
+  if (!calls || n_calls < 1 || n_calls > KVQ_MAX_BATCH) return KVQ_ERR_INVALID;
+  long long groups = 0;
+  for (int i = 0; i < n_calls; ++i) {
+    const int st = check_call(&calls[i], &out[i]);
+    if (st) return st;
+    const kvq_cache& c0 = *out[0].cache;
+    const kvq_cache& c = *out[i].cache;
+    if (c.head_dim != c0.head_dim || c.v_format != c0.v_format) return KVQ_ERR_UNSUPPORTED;
+    const int nb = c.head_dim / KVQ_BLOCK;
+    const bool rows0 = out[0].n_qtok * (out[0].n_q_heads / c0.n_kv_heads) * nb > 16;
+    const bool rows = out[i].n_qtok * (out[i].n_q_heads / c.n_kv_heads) * nb > 16;
+    if (rows != rows0) return KVQ_ERR_UNSUPPORTED;
+    groups += (long long)out[i].n_seq * c.n_kv_heads;
+  }
+  if (groups >= 256) {
+    for (int i = 0; i < n_calls; ++i)
+      plans[i] = kvq::plan_splits(*out[i].cache, out[i].n_seq, out[i].n_qtok, out[i].n_q_heads,
+                                  out[i].max_seq_len);
+  } else {
+    int chunk = kvq::kChunkAlign;
+    for (;; chunk += kvq::kChunkAlign) {
+      long long wgs = 0;
+      int most = 0;
+      for (int i = 0; i < n_calls; ++i) {
+        const long long sp = (out[i].max_seq_len + chunk - 1) / chunk;
+        wgs += (long long)out[i].n_seq * out[i].cache->n_kv_heads * sp;
+        most = (int)std::max<long long>(most, sp);
+      }
+      if ((wgs <= 256 && most <= kvq::kMaxSplits) || chunk >= (1 << 20)) break;
+    }
+    for (int i = 0; i < n_calls; ++i)
+      plans[i] = {chunk, (out[i].max_seq_len + chunk - 1) / chunk};
+  }
+  size_t total = 0;
+  for (int i = 0; i < n_calls; ++i)
+    total += kvq::workspace_layout(*out[i].cache, out[i].n_seq, out[i].n_qtok, out[i].n_q_heads,
+                                   plans[i]).total;
+  *ws_bytes = total;
+  return KVQ_OK;
+}
+
 }  // namespace
+
+int attn_decode_packed_batch_workspace_size(const kvq_attn_call* calls, int n_calls, size_t* bytes) {
+  if (!bytes) return KVQ_ERR_INVALID;
+  kvq::AttnCall c[KVQ_MAX_BATCH];
+  kvq::SplitPlan plans[KVQ_MAX_BATCH];
+  return check_batch(calls, n_calls, c, plans, bytes);
+}
+
+int attn_decode_packed_batch(const kvq_attn_call* calls, int n_calls, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  kvq::AttnCall c[KVQ_MAX_BATCH];
+  kvq::SplitPlan plans[KVQ_MAX_BATCH];
+  size_t need = 0;
+  const int st = check_batch(calls, n_calls, c, plans, &need);
+  if (st) return st;
+  if (workspace_bytes < need || !workspace) return KVQ_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KVQ_ERR_INVALID;
+  return kvq::launch_attn_batch(c, plans, n_calls, workspace, static_cast<hipStream_t>(stream))
+             ? KVQ_ERR_HIP
+             : KVQ_OK;
+}
 
 int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n_seq, int n_qtok,
                        int n_q_heads, const int32_t* seg_table, int max_segs,

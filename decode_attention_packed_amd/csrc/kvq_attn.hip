@@ -103,7 +103,29 @@ struct AttnParams {
   float scale_log2;       // sm_scale * log2(e)
   int xcd_local;          // splits of a (sequence, kv head) share an XCD (see block_coords)
   int merge_launch;       // 1: the split merge runs as a second launch (k_split_merge)
+  int n_seq_groups;       // n_seq * n_kv_heads
 };
+
+// Several calls in one launch (attn_decode_packed_batch): call i runs
+// work-groups start[i] .. start[i] + count[i] - 1 of the grid; start[i] is a
+// multiple of 8, so a call's work-groups keep the XCD placement below, and
+// the work-groups that pad a call's range to a multiple of 8 do nothing.
+// mstart gives the same ranges for the split-merge launch (row layout).
+constexpr int kMaxBatch = KVQ_MAX_BATCH;
+struct AttnBatch {
+  AttnParams p[kMaxBatch];
+  int start[kMaxBatch + 1];
+  int count[kMaxBatch];
+  int mstart[kMaxBatch + 1];
+  int n;
+};
+__device__ __forceinline__ int batch_call(const int* start, int n, int blk) {
+  int i = 0;
+#pragma unroll
+  for (int k = 1; k < kMaxBatch; ++k)
+    if (k < n && blk >= start[k]) i = k;
+  return i;
+}
 
 // Work-groups go to the 8 XCDs round-robin by linear index.  When the number
 // of (sequence, kv head) groups is a multiple of 8, linear index b runs group
@@ -114,8 +136,7 @@ struct BlockCoords {
   int seq, kvh, split;
   bool off_xcd;   // this work-group does not sit on the XCD its group expects
 };
-__device__ __forceinline__ BlockCoords block_coords(const AttnParams& p) {
-  const int b = blockIdx.x;
+__device__ __forceinline__ BlockCoords block_coords(const AttnParams& p, int b) {
   int g, split;
   if (p.xcd_local) {
     const int k = b / kXcds;
@@ -957,7 +978,7 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
 }
 
 template <int D, int VF>
-__global__ __launch_bounds__(kThreads) void k_attn_rows(AttnParams p) {
+__device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
   constexpr int NT = D / 16;
@@ -974,7 +995,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_rows(AttnParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const BlockCoords bc = block_coords(p);
+  const BlockCoords bc = block_coords(p, blk);
   const int split = bc.split, kvh = bc.kvh, seq = bc.seq;
   const int L = p.seq_len[seq];
   const int n_split_seq = min((L + p.chunk - 1) / p.chunk, p.n_split);   // clamp: see k_split_merge
@@ -1218,7 +1239,7 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
 }
 
 template <int D, int VF>
-__global__ __launch_bounds__(kThreads) void k_attn_cols(AttnParams p) {
+__device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
   constexpr int NG = D / 16;
@@ -1235,7 +1256,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_cols(AttnParams p) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const BlockCoords bc = block_coords(p);
+  const BlockCoords bc = block_coords(p, blk);
   const int split = bc.split, kvh = bc.kvh, seq = bc.seq;
   const int L = p.seq_len[seq];
   const int n_split_seq = min((L + p.chunk - 1) / p.chunk, p.n_split);   // clamp: see k_split_merge
@@ -1335,13 +1356,13 @@ __global__ __launch_bounds__(kThreads) void k_attn_cols(AttnParams p) {
 // split s's maximum and sum, the weights exp2(m_s - M) / sum_s exp2(m_s - M)
 // l_s go through LDS, and each lane combines D/64 columns of the row.
 template <int D>
-__global__ __launch_bounds__(64) void k_split_merge(AttnParams p) {
+__device__ __forceinline__ void split_merge_body(const AttnParams& p, int blk) {
   constexpr int C = D / 64;   // columns per lane
   __shared__ float s_w[kMaxSplits];
   const int lane = threadIdx.x;
   const int R = p.rows, G = p.group;
-  const int r = blockIdx.x % R;
-  const int grp = blockIdx.x / R;   // sequence * n_kv_heads + kv head
+  const int r = blk % R;
+  const int grp = blk / R;   // sequence * n_kv_heads + kv head
   const int seq = grp / p.n_kv_heads, kvh = grp - seq * p.n_kv_heads;
   const int L = p.seq_len[seq];
   // (seq_len above max_seq_len breaks the call's contract; the clamp keeps
@@ -1376,6 +1397,37 @@ __global__ __launch_bounds__(64) void k_split_merge(AttnParams p) {
   for (int c = 0; c < C; ++c) dst[c] = acc[c];
 }
 
+template <int D, int VF>
+__global__ __launch_bounds__(kThreads) void k_attn_rows(AttnParams p) {
+  attn_rows_body<D, VF>(p, blockIdx.x);
+}
+template <int D, int VF>
+__global__ __launch_bounds__(kThreads) void k_attn_cols(AttnParams p) {
+  attn_cols_body<D, VF>(p, blockIdx.x);
+}
+template <int D>
+__global__ __launch_bounds__(64) void k_split_merge(AttnParams p) {
+  split_merge_body<D>(p, blockIdx.x);
+}
+template <int D, int VF>
+__global__ __launch_bounds__(kThreads) void k_attn_rows_batch(AttnBatch b) {
+  const int i = batch_call(b.start, b.n, blockIdx.x);
+  const int blk = blockIdx.x - b.start[i];
+  if (blk < b.count[i]) attn_rows_body<D, VF>(b.p[i], blk);
+}
+template <int D, int VF>
+__global__ __launch_bounds__(kThreads) void k_attn_cols_batch(AttnBatch b) {
+  const int i = batch_call(b.start, b.n, blockIdx.x);
+  const int blk = blockIdx.x - b.start[i];
+  if (blk < b.count[i]) attn_cols_body<D, VF>(b.p[i], blk);
+}
+template <int D>
+__global__ __launch_bounds__(64) void k_split_merge_batch(AttnBatch b) {
+  const int i = batch_call(b.mstart, b.n, blockIdx.x);
+  const int blk = blockIdx.x - b.mstart[i];
+  if (blk < b.p[i].n_seq_groups * b.p[i].rows) split_merge_body<D>(b.p[i], blk);
+}
+
 bool attn_supported(int head_dim, int v_format) {
   return (head_dim == 128 || (!kF16K && head_dim == 64)) && (v_format == 0 || v_format == 1);
 }
@@ -1399,10 +1451,11 @@ static void launch_attn_kernel(AttnParams p, dim3 grid, hipStream_t stream) {
   }
 }
 
-int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
-                const int32_t* seg_table, int max_segs, const int32_t* seq_len,
-                const SplitPlan& plan, float sm_scale, int causal, void* workspace,
-                const float* k_new, const float* v_new, int n_new, hipStream_t stream) {
+static AttnParams make_params(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok,
+                              int n_q_heads, const int32_t* seg_table, int max_segs,
+                              const int32_t* seq_len, const SplitPlan& plan, float sm_scale,
+                              int causal, void* workspace, const float* k_new, const float* v_new,
+                              int n_new) {
   AttnParams p;
   const WorkspaceLayout ws = workspace_layout(c, n_seq, n_qtok, n_q_heads, plan);
   char* base = static_cast<char*>(workspace);
@@ -1431,9 +1484,19 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
   p.n_split = plan.n_split;
   p.causal = causal;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
-  const long long n_groups = (long long)n_seq * c.n_kv_heads;
-  p.xcd_local = n_groups % kXcds == 0;
-  const dim3 grid((unsigned)(n_groups * plan.n_split));
+  p.n_seq_groups = n_seq * c.n_kv_heads;
+  p.xcd_local = p.n_seq_groups % kXcds == 0;
+  p.merge_launch = 0;
+  return p;
+}
+
+int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
+                const int32_t* seg_table, int max_segs, const int32_t* seq_len,
+                const SplitPlan& plan, float sm_scale, int causal, void* workspace,
+                const float* k_new, const float* v_new, int n_new, hipStream_t stream) {
+  const AttnParams p = make_params(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
+                                   plan, sm_scale, causal, workspace, k_new, v_new, n_new);
+  const dim3 grid((unsigned)((long long)p.n_seq_groups * plan.n_split));
   if (c.head_dim == 128) {
     if (c.v_format == 0)
       launch_attn_kernel<128, 0>(p, grid, stream);
@@ -1449,6 +1512,56 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
   }
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
+
+#if KVQ_KFMT == 0
+template <int D, int VF>
+static void launch_batch_kernels(AttnBatch& b, bool rows, hipStream_t stream) {
+  if (!rows) {
+    hipLaunchKernelGGL((k_attn_cols_batch<D, VF>), dim3((unsigned)b.start[b.n]), dim3(kThreads), 0, stream, b);
+    return;
+  }
+  bool merge = false;
+  for (int i = 0; i < b.n; ++i) {
+    b.p[i].merge_launch = b.p[i].n_split > 1;
+    merge = merge || b.p[i].merge_launch;
+  }
+  hipLaunchKernelGGL((k_attn_rows_batch<D, VF>), dim3((unsigned)b.start[b.n]), dim3(kThreads), 0, stream, b);
+  if (merge)
+    hipLaunchKernelGGL((k_split_merge_batch<D>), dim3((unsigned)b.mstart[b.n]), dim3(64), 0, stream, b);
+}
+
+int launch_attn_batch(const AttnCall* calls, const SplitPlan* plans, int n_calls, void* workspace,
+                      hipStream_t stream) {
+  AttnBatch b;
+  b.n = n_calls;
+  b.start[0] = 0;
+  b.mstart[0] = 0;
+  char* base = static_cast<char*>(workspace);
+  for (int i = 0; i < n_calls; ++i) {
+    const AttnCall& a = calls[i];
+    b.p[i] = make_params(*a.cache, a.q, a.out, a.n_seq, a.n_qtok, a.n_q_heads, a.seg_table, a.max_segs,
+                         a.seq_len, plans[i], a.sm_scale, a.causal, base, nullptr, nullptr, 0);
+    base += workspace_layout(*a.cache, a.n_seq, a.n_qtok, a.n_q_heads, plans[i]).total;
+    b.count[i] = b.p[i].n_seq_groups * plans[i].n_split;
+    b.start[i + 1] = b.start[i] + (b.count[i] + kXcds - 1) / kXcds * kXcds;
+    b.mstart[i + 1] = b.mstart[i] + b.p[i].n_seq_groups * b.p[i].rows;
+  }
+  const kvq_cache& c = *calls[0].cache;
+  const bool rows = b.p[0].rows * (c.head_dim / kBlock) > 16;
+  if (c.head_dim == 128) {
+    if (c.v_format == 0)
+      launch_batch_kernels<128, 0>(b, rows, stream);
+    else
+      launch_batch_kernels<128, 1>(b, rows, stream);
+  } else {
+    if (c.v_format == 0)
+      launch_batch_kernels<64, 0>(b, rows, stream);
+    else
+      launch_batch_kernels<64, 1>(b, rows, stream);
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+#endif
 
 #if KVQ_KFMT == 1
 }  // namespace f16k

@@ -48,6 +48,25 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
                 const float* k_new, const float* v_new, int n_new, hipStream_t stream);
 
+// One call of a batched launch (attn_decode_packed_batch), validated.
+struct AttnCall {
+  const kvq_cache* cache;
+  const float* q;
+  float* out;
+  int n_seq, n_qtok, n_q_heads;
+  const int32_t* seg_table;
+  int max_segs;
+  const int32_t* seq_len;
+  int max_seq_len;
+  float sm_scale;
+  int causal;
+};
+
+// All calls share head_dim, V format and layout (column or row); call i uses
+// plans[i] and the workspace bytes after those of calls 0 .. i-1.
+int launch_attn_batch(const AttnCall* calls, const SplitPlan* plans, int n_calls, void* workspace,
+                      hipStream_t stream);
+
 // The same attention kernels compiled for fp16 K rows (kvq_attn_f16k.hip):
 // head_dim 128, column layout (query rows x 4 blocks <= 16), no append.
 namespace f16k {

@@ -40,6 +40,7 @@ extern "C" {
 #define KVQ_SEG_ALIGN 64        /* seg_tokens must be a positive multiple of this */
 #define KVQ_MAX_QTOK 16         /* query tokens x query heads per kv head, at most */
 #define KVQ_MAX_APPEND 16       /* tokens one fused append-and-attend call appends per sequence */
+#define KVQ_MAX_BATCH 4         /* calls one attn_decode_packed_batch launch runs */
 
 enum kvq_status {
   KVQ_OK = 0,
@@ -196,6 +197,41 @@ int attn_decode_packed_append(const kvq_cache* cache, const float* q, const floa
  */
 int kvq_debug_quant_q(const float* q, int n_rows, int head_dim, int8_t* codes, float* scales,
                       void* stream);
+/*
+ * attn_decode_packed_batch: several attn_decode_packed calls in one launch.
+ * Page 1's speculative-verify step attends over two caches per step (the
+ * main model's and the draft's); one launch lets the two overlap their fixed
+ * latencies (start-up, split merge) instead of paying them in turn.
+ *   calls    n_calls (1 .. KVQ_MAX_BATCH) call descriptions, each with the
+ *            meaning, layout and checks of attn_decode_packed's arguments
+ *            (host memory; read during the call only)
+ * Every call's cache must have the same head_dim and V format, and every
+ * call the same MFMA layout (query rows x 32-blocks <= 16 for all calls, or
+ * > 16 for all), else KVQ_ERR_UNSUPPORTED.  The workspace holds each call's
+ * workspace in turn (attn_decode_packed_batch_workspace_size); the split
+ * plan is made for the whole launch, so the bytes differ from the separate
+ * calls'.  The result of each call is that of attn_decode_packed up to
+ * rounding (the split points may differ).  Errors before any launch.
+ */
+typedef struct kvq_attn_call {
+  const kvq_cache* cache;
+  const float* q;
+  float* out;
+  int32_t n_seq;
+  int32_t n_qtok;
+  int32_t n_q_heads;
+  const int32_t* seg_table;
+  int32_t max_segs;
+  const int32_t* seq_len;
+  int32_t max_seq_len;
+  float sm_scale;
+  int32_t causal;
+} kvq_attn_call;
+
+int attn_decode_packed_batch_workspace_size(const kvq_attn_call* calls, int n_calls, size_t* bytes);
+int attn_decode_packed_batch(const kvq_attn_call* calls, int n_calls, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /*
  * fp16-K reference for A/B measurements (not the method).  Page 1 compares
  * its packed int8 K with K kept as fp16; these calls run the same attention

@@ -158,3 +158,37 @@ def test_f16k_reference_args_rejected():
     n = ctypes.c_size_t(0)
     assert L.attn_decode_f16k_workspace_size(ctypes.byref(c), 1, 1, 32, 1024, ctypes.byref(n)) == K.KVQ_OK
     assert n.value > 0
+
+
+def test_batch_args_rejected():
+    """attn_decode_packed_batch validates every call and the batch before any
+    launch: one head_dim, V format and MFMA layout for all calls."""
+    L = K.lib()
+    c128 = _fake_cache()
+    c64 = _fake_cache(head_dim=64)
+    cq8 = _fake_cache(v_format=1)
+
+    def call(cache, n_qtok=1, hq=32):
+        return K._lib.KvqAttnCallStruct(ctypes.pointer(cache), 0x5000, 0x6000, 1, n_qtok, hq, None, 1,
+                                        0x7000, 1024, 0.1, 0)
+
+    def run(calls, ws_bytes=1 << 30):
+        arr = (K._lib.KvqAttnCallStruct * max(1, len(calls)))(*calls)
+        return L.attn_decode_packed_batch(arr, len(calls), 0x8000, ws_bytes, None)
+
+    def size(calls):
+        arr = (K._lib.KvqAttnCallStruct * max(1, len(calls)))(*calls)
+        n = ctypes.c_size_t(0)
+        return L.attn_decode_packed_batch_workspace_size(arr, len(calls), ctypes.byref(n)), n.value
+
+    assert run([]) == K.KVQ_ERR_INVALID
+    assert run([call(c128)] * (K.KVQ_MAX_BATCH + 1)) == K.KVQ_ERR_INVALID
+    assert run([call(c128), call(c64)]) == K.KVQ_ERR_UNSUPPORTED        # head_dim differs
+    assert run([call(c128), call(cq8)]) == K.KVQ_ERR_UNSUPPORTED        # V format differs
+    assert run([call(c128), call(c128, n_qtok=4)]) == K.KVQ_ERR_UNSUPPORTED   # layouts differ
+    assert run([call(c128), call(c128, hq=12)]) == K.KVQ_ERR_INVALID    # a bad call
+    st, one = size([call(c128)])
+    assert st == K.KVQ_OK and one > 0
+    st, two = size([call(c128), call(c128, hq=16)])
+    assert st == K.KVQ_OK and two > one
+    assert run([call(c128), call(c128, hq=16)], ws_bytes=two - 16) == K.KVQ_ERR_WORKSPACE
