@@ -74,12 +74,14 @@ SplitPlan plan_splits(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads, 
     const long long n_groups = (long long)n_seq * c.n_kv_heads;
     chunk = kChunkAlign;
     if (n_groups >= target_groups) {
-      // Enough (sequence, kv head) groups to fill the GPU unsplit: split
-      // the longest sequences at most in two, so a batch of mixed lengths
-      // is not cut into many short work-groups whose start-up latency and
-      // merges then dominate (ragged batch: 94 us against 127 us with
-      // 2048-token chunks).
-      while (chunk < (1 << 20) && splits(chunk) > 2) chunk *= 2;
+      // Enough (sequence, kv head) groups to fill the GPU unsplit.  More,
+      // shorter work-groups only add start-up latency and merges, so the
+      // longest sequence splits just enough for about two groups' worth of
+      // work-groups per CU: in two below 512 groups, not at all from 512
+      // (ragged batch, 512 groups: 94 us unsplit, 107 us in two, 135 us in
+      // 4096-token chunks).
+      const long long most = std::max<long long>(1, 2 * target_groups / n_groups);
+      while (chunk < (1 << 20) && splits(chunk) > most) chunk *= 2;
     } else {
       // Few groups: grow the chunk while at least one work-group per CU
       // remains and the longest sequence still spreads over 8 or more.
