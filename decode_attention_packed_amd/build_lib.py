@@ -18,7 +18,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libkvq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_attn.hip", "kvq_attn_f16k.hip", "kvq_debug.hip"]
+SOURCES = ["kvq_api.cpp", "kvq_append.hip", "kvq_attn.hip", "kvq_attn_f16k.hip", "kvq_attn_w12.hip",
+           "kvq_debug.hip"]
 CFLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           # keep MFMA accumulators in VGPRs (no AGPR copies around each MFMA)

@@ -30,8 +30,8 @@
 //          score exceeds it.
 //   P.V    computed transposed, v_mfma_f32_16x16x32_f16 with A = 16 dims of
 //          V codes (exact fp16 integers from a byte permute and one packed
-//          f16 add) and B = p * d_v of the column's block, split into fp16
-//          hi + lo (about 22 bits).  V tiles are stored token-interleaved
+//          f16 add) and B = p * d_v of the column's block rounded to fp16
+//          (fp32 accumulation).  V tiles are stored token-interleaved
 //          ("BitLLM" page 3: the layout follows the reduction axis, T for
 //          S.V), so one 8-byte read is 8 tokens of one dim.
 //
@@ -50,18 +50,25 @@
 
 #include <type_traits>
 
-// KVQ_KFMT selects the K format this file is compiled for: 0 is the packed
-// int8 K of the method; 1 is K kept as fp16 rows, the unpacked baseline page 1
-// compares against (A/B reference only, compiled from kvq_attn_f16k.hip into
-// namespace kvq::f16k, column layout and head_dim 128 only).  Its K tiles are
-// twice as large, so that build runs 6 waves with 2 ring slots each.
+// This file is compiled three times.  The plain build (8 waves per
+// work-group) serves every call.  KVQ_NS names the namespace of the other two:
+//  - kvq::f16k (kvq_attn_f16k.hip): KVQ_KFMT 1 keeps K as fp16 rows, the
+//    unpacked baseline page 1 compares against (A/B reference only, column
+//    layout and head_dim 128 only).  Its K tiles are twice as large, so that
+//    build runs 6 waves with 2 ring slots each.
+//  - kvq::w12 (kvq_attn_w12.hip): KVQ_COLS_Q4_128 builds only the column
+//    kernel for q4_0 V at head_dim 128, with 12 waves (3 per SIMD) and 2 ring
+//    slots each; the plain build hands those calls to it.
 #ifndef KVQ_KFMT
 #define KVQ_KFMT 0
 #endif
+#ifndef KVQ_COLS_Q4_128
+#define KVQ_COLS_Q4_128 0
+#endif
 
 namespace kvq {
-#if KVQ_KFMT == 1
-namespace f16k {
+#ifdef KVQ_NS
+namespace KVQ_NS {
 #endif
 
 #ifndef KVQ_WAVES
@@ -652,6 +659,16 @@ __device__ __forceinline__ void split_f16_pair(float p0, float p1, uint32_t dpai
       : "v"(p0), "v"(p1), "v"(dpair));
 }
 
+// p * d rounded once to fp16, for two tokens at once: the P.V operand of the
+// column layout (11 significant bits; the weighted sum keeps fp32 MFMA
+// accumulation).  The row layout keeps the hi + lo pair above.
+__device__ __forceinline__ void round_f16_pair(float p0, float p1, uint32_t dpair, uint32_t& hi) {
+  asm("v_fma_mixlo_f16 %0, %1, %3, 0 op_sel_hi:[0,1,0]\n\t"
+      "v_fma_mixhi_f16 %0, %2, %3, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
+      : "=&v"(hi)
+      : "v"(p0), "v"(p1), "v"(dpair));
+}
+
 // Publish this work-group's partial and, in the last work-group of the
 // (sequence, kv head), merge every split into the output rows.  On entry
 // s_buf holds each wave's unnormalized rows ([wave][16][D]) followed by their
@@ -1192,7 +1209,7 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
     st.l += pj[j];
   }
 
-  // ---- B operand: p * d_v of this column's block as fp16 hi + lo
+  // ---- B operand: p * d_v of this column's block, rounded to fp16
   const uint4 dvw = *reinterpret_cast<const uint4*>(slot + S::DV_OFF + b * 64 + 16 * grp);
   uint32_t dv[4] = {dvw.x, dvw.y, dvw.z, dvw.w};
   if (!full) {
@@ -1202,11 +1219,10 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
     for (int j = 0; j < 8; ++j)
       if (j >= lim) dv[j >> 1] &= (j & 1) ? 0x0000FFFFu : 0xFFFF0000u;
   }
-  uint32_t hw[4], lw[4];
+  uint32_t hw[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) split_f16_pair(pj[2 * k], pj[2 * k + 1], dv[k], hw[k], lw[k]);
-  const v8h bhi = __builtin_bit_cast(v8h, hw);
-  const v8h blo = __builtin_bit_cast(v8h, lw);
+  for (int k = 0; k < 4; ++k) round_f16_pair(pj[2 * k], pj[2 * k + 1], dv[k], hw[k]);
+  const v8h bpv = __builtin_bit_cast(v8h, hw);
 
   // ---- (P.V)^T: A = V codes of dims 16g + col, tokens 8*grp .. +8
   if constexpr (VF == 0) {
@@ -1220,10 +1236,8 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
           slot + S::V_OFF + (R * 2 + ((grp >> 1) ^ ((R >> 2) & 1))) * 16 + 8 * (grp & 1));
       const v8h alo = bytes_to_f16x8(w.x & 0x0F0F0F0Fu, w.y & 0x0F0F0F0Fu, (_Float16)1032.0f);
       const v8h ahi = bytes_to_f16x8(w.x & 0xF0F0F0F0u, w.y & 0xF0F0F0F0u, (_Float16)1152.0f);
-      st.acc[2 * bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bhi, st.acc[2 * bb], 0, 0, 0);
-      st.acc[2 * bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, blo, st.acc[2 * bb], 0, 0, 0);
-      st.acc[2 * bb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bhi, st.acc[2 * bb + 1], 0, 0, 0);
-      st.acc[2 * bb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, blo, st.acc[2 * bb + 1], 0, 0, 0);
+      st.acc[2 * bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bpv, st.acc[2 * bb], 0, 0, 0);
+      st.acc[2 * bb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bpv, st.acc[2 * bb + 1], 0, 0, 0);
     }
   } else {
 #pragma unroll
@@ -1233,8 +1247,7 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
           slot + S::V_OFF + (R * 2 + ((grp >> 1) ^ ((R >> 2) & 1))) * 16 + 8 * (grp & 1));
       // int8 code c -> byte c ^ 0x80 = c + 128 -> fp16 (1024 + c + 128) - 1152
       const v8h av = bytes_to_f16x8(w.x ^ 0x80808080u, w.y ^ 0x80808080u, (_Float16)1152.0f);
-      st.acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bhi, st.acc[g], 0, 0, 0);
-      st.acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, blo, st.acc[g], 0, 0, 0);
+      st.acc[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bpv, st.acc[g], 0, 0, 0);
     }
   }
 }
@@ -1502,10 +1515,19 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
                 const int32_t* seg_table, int max_segs, const int32_t* seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
                 const float* k_new, const float* v_new, int n_new, hipStream_t stream) {
+#if KVQ_KFMT == 0 && !KVQ_COLS_Q4_128
+  // the column layout with q4_0 V at head_dim 128 runs the 12-wave build
+  if (c.head_dim == 128 && c.v_format == 0 && n_qtok * (n_q_heads / c.n_kv_heads) * (128 / kBlock) <= 16)
+    return w12::launch_attn(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len, plan,
+                            sm_scale, causal, workspace, k_new, v_new, n_new, stream);
+#endif
   const AttnParams p = make_params(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
                                    plan, sm_scale, causal, workspace, k_new, v_new, n_new);
   const dim3 grid((unsigned)((long long)p.n_seq_groups * plan.n_split));
-  if (c.head_dim == 128) {
+  if constexpr (KVQ_COLS_Q4_128) {
+    if (c.head_dim != 128 || c.v_format != 0) return -4;   // not reached: only those calls come here
+    hipLaunchKernelGGL((k_attn_cols<128, 0>), grid, dim3(kThreads), 0, stream, p);
+  } else if (c.head_dim == 128) {
     if (c.v_format == 0)
       launch_attn_kernel<128, 0>(p, grid, stream);
     else
@@ -1521,7 +1543,7 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-#if KVQ_KFMT == 0
+#if KVQ_KFMT == 0 && !KVQ_COLS_Q4_128
 template <int D, int VF>
 static void launch_batch_kernels(AttnBatch& b, bool rows, hipStream_t stream) {
   if (!rows) {
@@ -1571,7 +1593,7 @@ int launch_attn_batch(const AttnCall* calls, const SplitPlan* plans, int n_calls
 }
 #endif
 
-#if KVQ_KFMT == 1
-}  // namespace f16k
+#ifdef KVQ_NS
+}  // namespace KVQ_NS
 #endif
 }  // namespace kvq

@@ -4,4 +4,5 @@
 // slots each, as an fp16 K tile (8 KB) is twice the packed one.
 #define KVQ_KFMT 1
 #define KVQ_WAVES 6
+#define KVQ_NS f16k
 #include "kvq_attn.hip"

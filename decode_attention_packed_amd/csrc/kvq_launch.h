@@ -67,6 +67,15 @@ struct AttnCall {
 int launch_attn_batch(const AttnCall* calls, const SplitPlan* plans, int n_calls, void* workspace,
                       hipStream_t stream);
 
+// The column-layout kernel for q4_0 V at head_dim 128 built with 12 waves per
+// work-group (kvq_attn_w12.hip); launch_attn above hands those calls to it.
+namespace w12 {
+int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
+                const int32_t* seg_table, int max_segs, const int32_t* seq_len,
+                const SplitPlan& plan, float sm_scale, int causal, void* workspace,
+                const float* k_new, const float* v_new, int n_new, hipStream_t stream);
+}  // namespace w12
+
 // The same attention kernels compiled for fp16 K rows (kvq_attn_f16k.hip):
 // head_dim 128, column layout (query rows x 4 blocks <= 16), no append.
 namespace f16k {
