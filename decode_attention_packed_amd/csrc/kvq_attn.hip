@@ -108,9 +108,9 @@ struct AttnParams {
   int n_split;
   int causal;
   float scale_log2;       // sm_scale * log2(e)
-  int xcd_local;          // splits of a (sequence, kv head) share an XCD (see block_coords)
   int merge_launch;       // 1: the split merge runs as a second launch (k_split_merge)
   int n_seq_groups;       // n_seq * n_kv_heads
+  int n_groups_pad;       // n_seq_groups rounded up to a multiple of 8 (see block_coords)
 };
 
 // Several calls in one launch (attn_decode_packed_batch): call i runs
@@ -134,32 +134,30 @@ __device__ __forceinline__ int batch_call(const int* start, int n, int blk) {
   return i;
 }
 
-// Work-groups go to the 8 XCDs round-robin by linear index.  When the number
-// of (sequence, kv head) groups is a multiple of 8, linear index b runs group
-// (b % 8) + 8 * ((b / 8) / n_split), split (b / 8) % n_split, so all splits of
-// a group land on one XCD and share its L2; otherwise groups are consecutive.
+// Work-groups go to the 8 XCDs round-robin by linear index.  The grid holds
+// n_groups_pad (a multiple of 8) groups of n_split work-groups: linear index
+// b runs group (b % 8) + 8 * ((b / 8) / n_split), split (b / 8) % n_split, so
+// all splits of a group land on one XCD and the split merge reads partials
+// its L2 holds.  (An agent-scope acquire does not drop stale lines of
+// ordinary device memory from another XCD's L2, so partials must not cross
+// XCDs; groups past n_seq_groups only pad the grid and do nothing.)
 constexpr int kXcds = 8;
 struct BlockCoords {
   int seq, kvh, split;
+  bool pad;       // a padding work-group: returns at once
   bool off_xcd;   // this work-group does not sit on the XCD its group expects
 };
 __device__ __forceinline__ BlockCoords block_coords(const AttnParams& p, int b) {
-  int g, split;
-  if (p.xcd_local) {
-    const int k = b / kXcds;
-    g = b % kXcds + kXcds * (k / p.n_split);
-    split = k % p.n_split;
-  } else {
-    g = b / p.n_split;
-    split = b % p.n_split;
-  }
+  const int k = b / kXcds;
+  const int g = b % kXcds + kXcds * (k / p.n_split);
   unsigned xcc;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
   BlockCoords c;
-  c.seq = g / p.n_kv_heads;
-  c.kvh = g - c.seq * p.n_kv_heads;
-  c.split = split;
-  c.off_xcd = !p.xcd_local || (int)(xcc & 0xF) != b % kXcds;
+  c.pad = g >= p.n_seq_groups;
+  c.seq = c.pad ? 0 : g / p.n_kv_heads;
+  c.kvh = c.pad ? 0 : g - c.seq * p.n_kv_heads;
+  c.split = k % p.n_split;
+  c.off_xcd = (int)(xcc & 0xF) != b % kXcds;
   return c;
 }
 
@@ -1014,6 +1012,7 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const BlockCoords bc = block_coords(p, blk);
+  if (bc.pad) return;
   const int split = bc.split, kvh = bc.kvh, seq = bc.seq;
   const int L = p.seq_len[seq];
   const int n_split_seq = min((L + p.chunk - 1) / p.chunk, p.n_split);   // clamp: see k_split_merge
@@ -1271,6 +1270,7 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
   const BlockCoords bc = block_coords(p, blk);
+  if (bc.pad) return;
   const int split = bc.split, kvh = bc.kvh, seq = bc.seq;
   const int L = p.seq_len[seq];
   const int n_split_seq = min((L + p.chunk - 1) / p.chunk, p.n_split);   // clamp: see k_split_merge
@@ -1453,23 +1453,30 @@ bool attn_supported(int head_dim, int v_format) {
   return (head_dim == 128 || (!kF16K && head_dim == 64)) && (v_format == 0 || v_format == 1);
 }
 
+// The fused split merge relies on the whole device's 8 XCDs taking
+// work-groups round-robin (all splits of a group on one XCD, block_coords);
+// a device partitioned into fewer XCDs (fewer than 256 CUs on gfx950) runs
+// the merge as a second launch instead.
+static bool fused_merge_ok() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
+  return cus == 32 * kXcds;
+}
+
 template <int D, int VF>
 static void launch_attn_kernel(AttnParams p, dim3 grid, hipStream_t stream) {
-  if constexpr (kF16K) {
-    // column layout only (the caller checks rows * blocks <= 16)
-    p.merge_launch = 0;
-    hipLaunchKernelGGL((k_attn_cols<D, VF>), grid, dim3(kThreads), 0, stream, p);
-  } else if (p.rows * (D / kBlock) <= 16) {
-    p.merge_launch = 0;
+  const dim3 merge_grid((unsigned)((long long)p.n_seq_groups * p.rows));
+  if (kF16K || p.rows * (D / kBlock) <= 16) {
+    // column layout (the fp16-K build has no other): the split merge runs in
+    // the last work-group of each group, which needs the 8-XCD placement
+    p.merge_launch = p.n_split > 1 && !fused_merge_ok();
     hipLaunchKernelGGL((k_attn_cols<D, VF>), grid, dim3(kThreads), 0, stream, p);
   } else {
     p.merge_launch = p.n_split > 1;
     hipLaunchKernelGGL((k_attn_rows<D, VF>), grid, dim3(kThreads), 0, stream, p);
-    if (p.merge_launch) {
-      const long long n_groups = grid.x / p.n_split;
-      hipLaunchKernelGGL((k_split_merge<D>), dim3((unsigned)(n_groups * p.rows)), dim3(64), 0, stream, p);
-    }
   }
+  if (p.merge_launch) hipLaunchKernelGGL((k_split_merge<D>), merge_grid, dim3(64), 0, stream, p);
 }
 
 static AttnParams make_params(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok,
@@ -1506,7 +1513,7 @@ static AttnParams make_params(const kvq_cache& c, const float* q, float* out, in
   p.causal = causal;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   p.n_seq_groups = n_seq * c.n_kv_heads;
-  p.xcd_local = p.n_seq_groups % kXcds == 0;
+  p.n_groups_pad = (p.n_seq_groups + kXcds - 1) / kXcds * kXcds;
   p.merge_launch = 0;
   return p;
 }
@@ -1523,10 +1530,10 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
 #endif
   const AttnParams p = make_params(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
                                    plan, sm_scale, causal, workspace, k_new, v_new, n_new);
-  const dim3 grid((unsigned)((long long)p.n_seq_groups * plan.n_split));
+  const dim3 grid((unsigned)((long long)p.n_groups_pad * plan.n_split));
   if constexpr (KVQ_COLS_Q4_128) {
     if (c.head_dim != 128 || c.v_format != 0) return -4;   // not reached: only those calls come here
-    hipLaunchKernelGGL((k_attn_cols<128, 0>), grid, dim3(kThreads), 0, stream, p);
+    launch_attn_kernel<128, 0>(p, grid, stream);
   } else if (c.head_dim == 128) {
     if (c.v_format == 0)
       launch_attn_kernel<128, 0>(p, grid, stream);
@@ -1546,16 +1553,18 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
 #if KVQ_KFMT == 0 && !KVQ_COLS_Q4_128
 template <int D, int VF>
 static void launch_batch_kernels(AttnBatch& b, bool rows, hipStream_t stream) {
-  if (!rows) {
-    hipLaunchKernelGGL((k_attn_cols_batch<D, VF>), dim3((unsigned)b.start[b.n]), dim3(kThreads), 0, stream, b);
-    return;
-  }
+  // the column layout merges in its last work-groups where the device's 8
+  // XCDs take work-groups round-robin (launch_attn_kernel)
+  const bool fused = !rows && fused_merge_ok();
   bool merge = false;
   for (int i = 0; i < b.n; ++i) {
-    b.p[i].merge_launch = b.p[i].n_split > 1;
+    b.p[i].merge_launch = b.p[i].n_split > 1 && !fused;
     merge = merge || b.p[i].merge_launch;
   }
-  hipLaunchKernelGGL((k_attn_rows_batch<D, VF>), dim3((unsigned)b.start[b.n]), dim3(kThreads), 0, stream, b);
+  if (!rows)
+    hipLaunchKernelGGL((k_attn_cols_batch<D, VF>), dim3((unsigned)b.start[b.n]), dim3(kThreads), 0, stream, b);
+  else
+    hipLaunchKernelGGL((k_attn_rows_batch<D, VF>), dim3((unsigned)b.start[b.n]), dim3(kThreads), 0, stream, b);
   if (merge)
     hipLaunchKernelGGL((k_split_merge_batch<D>), dim3((unsigned)b.mstart[b.n]), dim3(64), 0, stream, b);
 }
@@ -1572,7 +1581,7 @@ int launch_attn_batch(const AttnCall* calls, const SplitPlan* plans, int n_calls
     b.p[i] = make_params(*a.cache, a.q, a.out, a.n_seq, a.n_qtok, a.n_q_heads, a.seg_table, a.max_segs,
                          a.seq_len, plans[i], a.sm_scale, a.causal, base, nullptr, nullptr, 0);
     base += workspace_layout(*a.cache, a.n_seq, a.n_qtok, a.n_q_heads, plans[i]).total;
-    b.count[i] = b.p[i].n_seq_groups * plans[i].n_split;
+    b.count[i] = b.p[i].n_groups_pad * plans[i].n_split;
     b.start[i + 1] = b.start[i] + (b.count[i] + kXcds - 1) / kXcds * kXcds;
     b.mstart[i + 1] = b.mstart[i] + b.p[i].n_seq_groups * b.p[i].rows;
   }

@@ -294,6 +294,34 @@ def test_workspace_reuse_across_shapes():
     assert not counters.any()
 
 
+def test_workspace_reuse_changing_inputs_odd_groups():
+    """Three kv heads (a group count that is not a multiple of 8) split many
+    ways, three calls with different queries on one workspace: every call
+    must match the oracle.  The split merge of a group reads the partials of
+    its other work-groups; they must all have run on one XCD, or the merge
+    can read lines an earlier call left in its L2."""
+    rng = np.random.default_rng(31)
+    L, Hkv, G, D = 16384, 3, 4, 128
+    spec = W.CacheSpec("odd3", 1, 1, Hkv * G, Hkv, D, L, W.V_Q4_0)
+    k = rng.standard_normal((1, L, Hkv, D)).astype(np.float32)
+    v = rng.standard_normal((1, L, Hkv, D)).astype(np.float32)
+    ci = W.CacheInputs(spec, rng.standard_normal((1, 1, Hkv * G, D)).astype(np.float32), k, v,
+                       np.array([L], np.int32), None, 1, L)
+    _say("workspace reuse, 3 kv heads, changing queries")
+    cache, table, max_segs = H.build_cache(ci)
+    need = K.attn_decode_packed_workspace_size(cache, 1, 1, Hkv * G, L)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    sl = torch.tensor([L], dtype=torch.int32, device="cuda")
+    for call in range(3):
+        ci.q = (rng.standard_normal(ci.q.shape) * (1.0 + call)).astype(np.float32)
+        q = H.dev(ci.q)
+        out = torch.empty_like(q)
+        K.attn_decode_packed(cache, q, out, sl, L, spec.sm_scale, False, ws)
+        torch.cuda.synchronize()
+        H.assert_close(out.cpu().numpy(), H.oracle_attention(ci), f"odd groups call {call}")
+    assert not ws[:4 * Hkv].cpu().numpy().any()
+
+
 def test_attention_errors_leave_output_untouched():
     ci = W.make_inputs("tiny", ctx=128)[0]
     cache, table, max_segs = H.build_cache(ci)
