@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "decode_attention_packed_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_long128k.txt")
 CALIB_BYTES = 256 << 20   # known sizes read / written by the calibration kernels
-ATTN_KERNEL = "kvq::k_attn_cols<128, 0>"   # not the fp16-K A/B build (kvq::f16k::)
+ATTN_KERNEL = "kvq::w12::k_attn_cols<128, 0>"   # the 12-wave build that runs the step
 
 
 def kernel_source_hash() -> str:

@@ -110,8 +110,12 @@ struct AttnParams {
   float scale_log2;       // sm_scale * log2(e)
   int merge_launch;       // 1: the split merge runs as a second launch (k_split_merge)
   int n_seq_groups;       // n_seq * n_kv_heads
-  int n_groups_pad;       // n_seq_groups rounded up to a multiple of 8 (see block_coords)
+  int xcd_local;          // all splits of a group on one XCD (see block_coords)
+  int n_groups_pad;       // groups in the grid: n_seq_groups, rounded up to 8 when xcd_local
 };
+
+// Chunks from which single calls run the 12-wave build (12 waves x 4 tiles).
+constexpr int kW12MinChunk = 12 * 4 * kTile;
 
 // Several calls in one launch (attn_decode_packed_batch): call i runs
 // work-groups start[i] .. start[i] + count[i] - 1 of the grid; start[i] is a
@@ -134,13 +138,17 @@ __device__ __forceinline__ int batch_call(const int* start, int n, int blk) {
   return i;
 }
 
-// Work-groups go to the 8 XCDs round-robin by linear index.  The grid holds
-// n_groups_pad (a multiple of 8) groups of n_split work-groups: linear index
-// b runs group (b % 8) + 8 * ((b / 8) / n_split), split (b / 8) % n_split, so
-// all splits of a group land on one XCD and the split merge reads partials
-// its L2 holds.  (An agent-scope acquire does not drop stale lines of
-// ordinary device memory from another XCD's L2, so partials must not cross
-// XCDs; groups past n_seq_groups only pad the grid and do nothing.)
+// Work-groups go to the 8 XCDs round-robin by linear index.  With xcd_local
+// the grid holds n_groups_pad (a multiple of 8) groups of n_split
+// work-groups: linear index b runs group (b % 8) + 8 * ((b / 8) / n_split),
+// split (b / 8) % n_split, so all splits of a group land on one XCD and the
+// fused split merge reads partials its own L2 holds.  (An agent-scope
+// acquire does not drop stale lines of ordinary device memory from another
+// XCD's L2, so a fused merge must not read partials across XCDs; groups past
+// n_seq_groups only pad the grid and do nothing.)  That placement is used
+// when the group count is a multiple of 8 or the grid is small; otherwise a
+// group's splits are consecutive work-groups spread over all XCDs, and the
+// split merge runs as a second launch.
 constexpr int kXcds = 8;
 struct BlockCoords {
   int seq, kvh, split;
@@ -148,16 +156,23 @@ struct BlockCoords {
   bool off_xcd;   // this work-group does not sit on the XCD its group expects
 };
 __device__ __forceinline__ BlockCoords block_coords(const AttnParams& p, int b) {
-  const int k = b / kXcds;
-  const int g = b % kXcds + kXcds * (k / p.n_split);
+  int g, split;
+  if (p.xcd_local) {
+    const int k = b / kXcds;
+    g = b % kXcds + kXcds * (k / p.n_split);
+    split = k % p.n_split;
+  } else {
+    g = b / p.n_split;
+    split = b % p.n_split;
+  }
   unsigned xcc;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
   BlockCoords c;
   c.pad = g >= p.n_seq_groups;
   c.seq = c.pad ? 0 : g / p.n_kv_heads;
   c.kvh = c.pad ? 0 : g - c.seq * p.n_kv_heads;
-  c.split = k % p.n_split;
-  c.off_xcd = (int)(xcc & 0xF) != b % kXcds;
+  c.split = split;
+  c.off_xcd = !p.xcd_local || (int)(xcc & 0xF) != b % kXcds;
   return c;
 }
 
@@ -1469,8 +1484,8 @@ static void launch_attn_kernel(AttnParams p, dim3 grid, hipStream_t stream) {
   const dim3 merge_grid((unsigned)((long long)p.n_seq_groups * p.rows));
   if (kF16K || p.rows * (D / kBlock) <= 16) {
     // column layout (the fp16-K build has no other): the split merge runs in
-    // the last work-group of each group, which needs the 8-XCD placement
-    p.merge_launch = p.n_split > 1 && !fused_merge_ok();
+    // the last work-group of each group when all its splits share an XCD
+    p.merge_launch = p.n_split > 1 && !(p.xcd_local && fused_merge_ok());
     hipLaunchKernelGGL((k_attn_cols<D, VF>), grid, dim3(kThreads), 0, stream, p);
   } else {
     p.merge_launch = p.n_split > 1;
@@ -1513,7 +1528,9 @@ static AttnParams make_params(const kvq_cache& c, const float* q, float* out, in
   p.causal = causal;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
   p.n_seq_groups = n_seq * c.n_kv_heads;
-  p.n_groups_pad = (p.n_seq_groups + kXcds - 1) / kXcds * kXcds;
+  // XCD-local placement when it costs no parallelism (see block_coords)
+  p.xcd_local = p.n_seq_groups % kXcds == 0 || (long long)p.n_seq_groups * plan.n_split <= 64;
+  p.n_groups_pad = p.xcd_local ? (p.n_seq_groups + kXcds - 1) / kXcds * kXcds : p.n_seq_groups;
   p.merge_launch = 0;
   return p;
 }
@@ -1524,7 +1541,9 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
                 const float* k_new, const float* v_new, int n_new, hipStream_t stream) {
 #if KVQ_KFMT == 0 && !KVQ_COLS_Q4_128
   // the column layout with q4_0 V at head_dim 128 runs the 12-wave build
-  if (c.head_dim == 128 && c.v_format == 0 && n_qtok * (n_q_heads / c.n_kv_heads) * (128 / kBlock) <= 16)
+  // when its chunks give every wave at least 4 tiles
+  if (c.head_dim == 128 && c.v_format == 0 && n_qtok * (n_q_heads / c.n_kv_heads) * (128 / kBlock) <= 16 &&
+      plan.chunk >= kW12MinChunk)
     return w12::launch_attn(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len, plan,
                             sm_scale, causal, workspace, k_new, v_new, n_new, stream);
 #endif
@@ -1558,7 +1577,7 @@ static void launch_batch_kernels(AttnBatch& b, bool rows, hipStream_t stream) {
   const bool fused = !rows && fused_merge_ok();
   bool merge = false;
   for (int i = 0; i < b.n; ++i) {
-    b.p[i].merge_launch = b.p[i].n_split > 1 && !fused;
+    b.p[i].merge_launch = b.p[i].n_split > 1 && !(fused && b.p[i].xcd_local);
     merge = merge || b.p[i].merge_launch;
   }
   if (!rows)
