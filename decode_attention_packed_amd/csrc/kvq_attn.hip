@@ -142,13 +142,12 @@ __device__ __forceinline__ int batch_call(const int* start, int n, int blk) {
 // the grid holds n_groups_pad (a multiple of 8) groups of n_split
 // work-groups: linear index b runs group (b % 8) + 8 * ((b / 8) / n_split),
 // split (b / 8) % n_split, so all splits of a group land on one XCD and the
-// fused split merge reads partials its own L2 holds.  (An agent-scope
-// acquire does not drop stale lines of ordinary device memory from another
-// XCD's L2, so a fused merge must not read partials across XCDs; groups past
-// n_seq_groups only pad the grid and do nothing.)  That placement is used
-// when the group count is a multiple of 8 or the grid is small; otherwise a
-// group's splits are consecutive work-groups spread over all XCDs, and the
-// split merge runs as a second launch.
+// fused split merge reads partials that passed through its own L2 (groups
+// past n_seq_groups only pad the grid and do nothing).  That placement is
+// used when the group count is a multiple of 8 or the grid is small, where
+// padding costs no parallelism; otherwise a group's splits are consecutive
+// work-groups spread over all XCDs, and the merge reads their write-through
+// partials after an agent-scope acquire.
 constexpr int kXcds = 8;
 struct BlockCoords {
   int seq, kvh, split;
@@ -359,38 +358,39 @@ __device__ __forceinline__ void wait_tiles(int pending) {
   }
 }
 
-// Tiles of a work-group's chunk are handed out in order: the first two of
-// each wave statically (wave w: tiles w and w + kWaves), the rest from an LDS
-// counter, so a wave that runs ahead takes more tiles.  One lane takes the
-// next index; the result is uniform.
-__device__ __forceinline__ int grab_tile(int* s_next, int c0) {
-  int i = 0;
-  if (__lane_id() == 0)
-    i = __hip_atomic_fetch_add(s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-  return c0 + kTile * __builtin_amdgcn_readfirstlane(i);
-}
+// Tiles of a work-group's chunk are dealt to its waves round-robin: wave w
+// takes tiles w, w + kWaves, w + 2 kWaves, ...  The assignment is fixed, so
+// every wave accumulates the same tiles in the same order on every run and
+// the output is bit-for-bit reproducible.  (Handing tiles out from an LDS
+// counter instead balanced nothing measurable and made each wave's tile set,
+// and with it the fp16 rounding of its P.V operand, vary from run to run.)
+constexpr int kWaveStride = kTile * kWaves;
 
 // A wave's tiles in flight: `cur` is the next one to process, `n1` was
-// issued after it, `g` is taken from the counter but not issued yet.  Tile
-// starts only grow, so once one is past the chunk end all later ones are.
+// issued after it, `g` is the one after `n1`, not issued yet.  Tile starts
+// only grow, so once one is past the chunk end all later ones are.
 struct TileQueue {
   int cur, n1, g;
 };
+__device__ __forceinline__ TileQueue first_tiles(int c0, int wave) {
+  const int t = c0 + kTile * wave;
+  return {t, t + kWaveStride, t + 2 * kWaveStride};
+}
 
 // One step of a wave's ring: refill and wait as the slot count allows, then
 // run `body` on the tile in slot SLOT (a compile-time slot, so LDS offsets
 // become immediates).  Returns false once the wave's tiles are done.
 template <int D, int VF, int SLOT, class Body>
-__device__ __forceinline__ bool ring_step(const AttnParams& p, int seq, int kvh, int c0, int c1,
-                                          int* s_next, uint32_t ring_lds, const TileLane<D, VF>& tl,
+__device__ __forceinline__ bool ring_step(const AttnParams& p, int seq, int kvh, int c1,
+                                          uint32_t ring_lds, const TileLane<D, VF>& tl,
                                           TileCursor& cur, TileQueue& q, Body& body) {
   using S = Slot<D, VF>;
   if (q.cur >= c1) return false;
   if constexpr (S::NSLOT == 3) {
-    // the grabbed tile goes into the slot freed last step
+    // the next tile goes into the slot freed last step
     const int n2 = q.g;
     if (n2 < c1) issue_tile<D, VF>(p, seq, kvh, n2, ring_lds + ((SLOT + 2) % 3) * S::BYTES, tl, cur);
-    q.g = grab_tile(s_next, c0);
+    q.g = n2 + kWaveStride;
     wait_tiles<S::LPT>((q.n1 < c1) + (n2 < c1));
     body(std::integral_constant<int, SLOT>{}, q.cur);
     q.cur = q.n1;
@@ -401,25 +401,25 @@ __device__ __forceinline__ bool ring_step(const AttnParams& p, int seq, int kvh,
     if (q.g < c1) issue_tile<D, VF>(p, seq, kvh, q.g, ring_lds + SLOT * S::BYTES, tl, cur);
     q.cur = q.n1;
     q.n1 = q.g;
-    q.g = grab_tile(s_next, c0);
+    q.g += kWaveStride;
   }
   return true;
 }
 
 // Run a wave's ring to the end.  On entry tile q.cur sits in slot 0 and
-// q.n1 in slot 1 (both issued or past the end), and q.g is taken.
+// q.n1 in slot 1 (both issued or past the end).
 template <int D, int VF, class Body>
-__device__ __forceinline__ void run_ring(const AttnParams& p, int seq, int kvh, int c0, int c1,
-                                         int* s_next, uint32_t ring_lds, const TileLane<D, VF>& tl,
+__device__ __forceinline__ void run_ring(const AttnParams& p, int seq, int kvh, int c1,
+                                         uint32_t ring_lds, const TileLane<D, VF>& tl,
                                          TileCursor& cur, TileQueue& q, Body& body) {
   if constexpr (Slot<D, VF>::NSLOT == 3) {
-    while (ring_step<D, VF, 0>(p, seq, kvh, c0, c1, s_next, ring_lds, tl, cur, q, body) &&
-           ring_step<D, VF, 1>(p, seq, kvh, c0, c1, s_next, ring_lds, tl, cur, q, body) &&
-           ring_step<D, VF, 2>(p, seq, kvh, c0, c1, s_next, ring_lds, tl, cur, q, body)) {
+    while (ring_step<D, VF, 0>(p, seq, kvh, c1, ring_lds, tl, cur, q, body) &&
+           ring_step<D, VF, 1>(p, seq, kvh, c1, ring_lds, tl, cur, q, body) &&
+           ring_step<D, VF, 2>(p, seq, kvh, c1, ring_lds, tl, cur, q, body)) {
     }
   } else {
-    while (ring_step<D, VF, 0>(p, seq, kvh, c0, c1, s_next, ring_lds, tl, cur, q, body) &&
-           ring_step<D, VF, 1>(p, seq, kvh, c0, c1, s_next, ring_lds, tl, cur, q, body)) {
+    while (ring_step<D, VF, 0>(p, seq, kvh, c1, ring_lds, tl, cur, q, body) &&
+           ring_step<D, VF, 1>(p, seq, kvh, c1, ring_lds, tl, cur, q, body)) {
     }
   }
 }
@@ -1020,7 +1020,6 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
 
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   __shared__ int s_last;
-  __shared__ int s_next;   // next dynamically handed-out tile of the chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1037,9 +1036,8 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   const int R = p.rows, G = p.group;
   const TileLane<D, VF> tl = tile_lane_offsets<D, VF>(lane);
   TileCursor cur = {-1, 0};
-  TileQueue tq = {c0 + kTile * wave, c0 + kTile * (wave + kWaves), 0};
+  TileQueue tq = first_tiles(c0, wave);
   const uint32_t ring_lds = lds_addr(s_lds + wave * S::NSLOT * S::BYTES);
-  if (tid == 0) s_next = 2 * kWaves;
 
   int8_t* s_qc;
   float* s_qd;
@@ -1060,7 +1058,6 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   }
   __syncthreads();   // every wave has its operands; wave 0's last slot is free
   if (S::NSLOT == 2 && tq.n1 < c1) issue_tile<D, VF>(p, seq, kvh, tq.n1, ring_lds + S::BYTES, tl, cur);
-  tq.g = grab_tile(&s_next, c0);
 
   WaveState<D> st;
 #pragma unroll
@@ -1077,7 +1074,7 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
     if (t0 + kTile > app.lo && t0 < app.hi) patch_tile<D, VF>(ring + SL * S::BYTES, s_patch, t0, app);
     process_tile<D, VF>(ring + SL * S::BYTES, pbuf, t0, c1, qa, dqs, vis, st);
   };
-  run_ring<D, VF>(p, seq, kvh, c0, c1, &s_next, ring_lds, tl, cur, tq, body);
+  run_ring<D, VF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
   if (app.hi > app.lo) write_appended<D, VF>(p, seq, kvh, app, s_patch);
 
   // ---- this wave's rows to LDS for the merge
@@ -1278,7 +1275,6 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
 
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   __shared__ int s_last;
-  __shared__ int s_next;   // next dynamically handed-out tile of the chunk
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1295,9 +1291,8 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   const int R = p.rows, G = p.group;
   const TileLane<D, VF> tl = tile_lane_offsets<D, VF>(lane);
   TileCursor cur = {-1, 0};
-  TileQueue tq = {c0 + kTile * wave, c0 + kTile * (wave + kWaves), 0};
+  TileQueue tq = first_tiles(c0, wave);
   const uint32_t ring_lds = lds_addr(s_lds + wave * S::NSLOT * S::BYTES);
-  if (tid == 0) s_next = 2 * kWaves;
 
   int8_t* s_qc;
   float* s_qd;
@@ -1327,7 +1322,6 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   const int vis_min = min(p.causal ? L - p.n_qtok + 1 : L, c1);   // the first query token's
   __syncthreads();   // every wave has its operands; wave 0's last slot is free
   if (S::NSLOT == 2 && tq.n1 < c1) issue_tile<D, VF>(p, seq, kvh, tq.n1, ring_lds + S::BYTES, tl, cur);
-  tq.g = grab_tile(&s_next, c0);
 
   ColState<D> st;
 #pragma unroll
@@ -1345,7 +1339,7 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
                              qb, wq, st);
     first = false;
   };
-  run_ring<D, VF>(p, seq, kvh, c0, c1, &s_next, ring_lds, tl, cur, tq, body);
+  run_ring<D, VF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
   if (app.hi > app.lo) write_appended<D, VF>(p, seq, kvh, app, s_patch);
 
   // ---- this wave's rows to LDS for the merge
@@ -1468,24 +1462,13 @@ bool attn_supported(int head_dim, int v_format) {
   return (head_dim == 128 || (!kF16K && head_dim == 64)) && (v_format == 0 || v_format == 1);
 }
 
-// The fused split merge relies on the whole device's 8 XCDs taking
-// work-groups round-robin (all splits of a group on one XCD, block_coords);
-// a device partitioned into fewer XCDs (fewer than 256 CUs on gfx950) runs
-// the merge as a second launch instead.
-static bool fused_merge_ok() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return false;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return false;
-  return cus == 32 * kXcds;
-}
-
 template <int D, int VF>
 static void launch_attn_kernel(AttnParams p, dim3 grid, hipStream_t stream) {
   const dim3 merge_grid((unsigned)((long long)p.n_seq_groups * p.rows));
   if (kF16K || p.rows * (D / kBlock) <= 16) {
     // column layout (the fp16-K build has no other): the split merge runs in
-    // the last work-group of each group when all its splits share an XCD
-    p.merge_launch = p.n_split > 1 && !(p.xcd_local && fused_merge_ok());
+    // the last work-group of each group
+    p.merge_launch = 0;
     hipLaunchKernelGGL((k_attn_cols<D, VF>), grid, dim3(kThreads), 0, stream, p);
   } else {
     p.merge_launch = p.n_split > 1;
@@ -1572,12 +1555,11 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
 #if KVQ_KFMT == 0 && !KVQ_COLS_Q4_128
 template <int D, int VF>
 static void launch_batch_kernels(AttnBatch& b, bool rows, hipStream_t stream) {
-  // the column layout merges in its last work-groups where the device's 8
-  // XCDs take work-groups round-robin (launch_attn_kernel)
-  const bool fused = !rows && fused_merge_ok();
+  // the column layout merges in the last work-group of each group, the row
+  // layout in a second launch (launch_attn_kernel)
   bool merge = false;
   for (int i = 0; i < b.n; ++i) {
-    b.p[i].merge_launch = b.p[i].n_split > 1 && !(fused && b.p[i].xcd_local);
+    b.p[i].merge_launch = rows && b.p[i].n_split > 1;
     merge = merge || b.p[i].merge_launch;
   }
   if (!rows)

@@ -267,12 +267,21 @@ def test_attention_verify128k_full_size():
         del cache
 
 
-def test_attention_deterministic():
-    ci = W.make_inputs("gqa8k")[0]
-    cache, table, max_segs = H.build_cache(ci)
-    a = H.run_attention(cache, ci, table, max_segs)
-    b = H.run_attention(cache, ci, table, max_segs)
-    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+@pytest.mark.parametrize("name,ctx", [("gqa8k", None), ("long128k", 65536), ("verify128k", 6000),
+                                      ("ragged", None)])
+def test_attention_deterministic(name, ctx):
+    """Repeated calls on the same inputs give bit-identical outputs: every
+    wave accumulates a fixed set of tiles in a fixed order, and the split
+    merge combines the partials in split order.  Covers the 8-wave and
+    12-wave column kernels (gqa8k, a 64k-token cache), the row layout with
+    its merge launch (the verify caches) and a wide ragged batch."""
+    for ci in W.make_inputs(name, ctx=ctx):
+        _say(f"determinism {ci.spec.name} ctx {ci.spec.ctx}")
+        cache, table, max_segs = H.build_cache(ci)
+        runs = [H.run_attention(cache, ci, table, max_segs) for _ in range(3)]
+        for r in runs[1:]:
+            assert np.array_equal(runs[0].view(np.uint32), r.view(np.uint32)), ci.spec.name
+        del cache
 
 
 def test_workspace_reuse_across_shapes():
@@ -297,9 +306,10 @@ def test_workspace_reuse_across_shapes():
 def test_workspace_reuse_changing_inputs_odd_groups():
     """Three kv heads (a group count that is not a multiple of 8) split many
     ways, three calls with different queries on one workspace: every call
-    must match the oracle.  The split merge of a group reads the partials of
-    its other work-groups; they must all have run on one XCD, or the merge
-    can read lines an earlier call left in its L2."""
+    must match the oracle.  The group's splits are spread over the XCDs, so
+    its split merge reads partials written through other XCDs' L2s after an
+    agent-scope acquire; lines an earlier call left in any L2 must not leak
+    into a later call's output."""
     rng = np.random.default_rng(31)
     L, Hkv, G, D = 16384, 3, 4, 128
     spec = W.CacheSpec("odd3", 1, 1, Hkv * G, Hkv, D, L, W.V_Q4_0)
