@@ -680,27 +680,19 @@ __device__ __forceinline__ v8h bytes_to_f16x8(uint32_t w0, uint32_t w1, _Float16
   return __builtin_bit_cast(v8h, r);
 }
 
-// p * d as an fp16 pair sum, for two tokens at once: hi = fp16(p*d),
-// lo = fp16(p*d - hi), each from one fused multiply-add in fp32 with a single
-// rounding (d is an fp16 pair, p two fp32 values); hi + lo keeps ~22 bits.
-__device__ __forceinline__ void split_f16_pair(float p0, float p1, uint32_t dpair, uint32_t& hi,
-                                               uint32_t& lo) {
-  asm("v_fma_mixlo_f16 %0, %2, %4, 0 op_sel_hi:[0,1,0]\n\t"
-      "v_fma_mixhi_f16 %0, %3, %4, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
-      "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel_hi:[0,1,1]\n\t"
-      "v_fma_mixhi_f16 %1, %3, %4, -%0 op_sel:[0,1,1] op_sel_hi:[0,1,1]"
-      : "=&v"(hi), "=&v"(lo)
-      : "v"(p0), "v"(p1), "v"(dpair));
-}
-
-// p * d rounded once to fp16, for two tokens at once: the P.V operand of the
-// column layout (11 significant bits; the weighted sum keeps fp32 MFMA
-// accumulation).  The row layout keeps the hi + lo pair above.
-__device__ __forceinline__ void round_f16_pair(float p0, float p1, uint32_t dpair, uint32_t& hi) {
-  asm("v_fma_mixlo_f16 %0, %1, %3, 0 op_sel_hi:[0,1,0]\n\t"
-      "v_fma_mixhi_f16 %0, %2, %3, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]"
-      : "=&v"(hi)
-      : "v"(p0), "v"(p1), "v"(dpair));
+// p * d as fp16, for two tokens at once (d is an fp16 pair, p two fp32
+// values): the P.V operand of both layouts, 11 significant bits, with the
+// weighted sum accumulated in fp32 by the MFMA.  Each product is formed in
+// fp32 by v_fma_mix_f32 and the pair rounded to fp16 by v_cvt_pk_f16_f32.
+// Written as plain arithmetic rather than inline assembly on purpose: the
+// compiler inserts the wait states an MFMA needs before a VALU instruction
+// overwrites a register the MFMA still reads as its accumulator input only
+// for instructions it emits itself, and it reuses such a dead accumulator
+// register for the next value right after the MFMA issues.
+__device__ __forceinline__ uint32_t round_f16_pair(float p0, float p1, uint32_t dpair) {
+  const v2h d = __builtin_bit_cast(v2h, dpair);
+  const v2h r = {(_Float16)__builtin_fmaf(p0, (float)d.x, 0.0f), (_Float16)__builtin_fmaf(p1, (float)d.y, 0.0f)};
+  return __builtin_bit_cast(uint32_t, r);
 }
 
 // Publish this work-group's partial and, in the last work-group of the
@@ -869,15 +861,12 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, 
 // Row layout
 // ---------------------------------------------------------------------------
 
-// wq * fp16 half (0 = low, 1 = high) of `pair`, in fp32 with one rounding.
+// wq * fp16 half (0 = low, 1 = high) of `pair`, in fp32 with one rounding
+// (one v_fma_mix_f32; plain arithmetic for the reason given at round_f16_pair).
 template <int HI>
 __device__ __forceinline__ float mul_f32_f16(float wq, uint32_t pair) {
-  float r;
-  if constexpr (HI)
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]" : "=v"(r) : "v"(wq), "v"(pair));
-  else
-    asm("v_fma_mix_f32 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(r) : "v"(wq), "v"(pair));
-  return r;
+  const v2h d = __builtin_bit_cast(v2h, pair);
+  return __builtin_fmaf(wq, (float)(HI ? d.y : d.x), 0.0f);
 }
 
 // Running state of one wave: output tiles (rows 4*(lane/16)+i, dims
@@ -993,23 +982,21 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     const uint32_t* dvw = reinterpret_cast<const uint32_t*>(&dv[b]);
-    uint32_t hw[4], lw[4];
+    uint32_t hw[4];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) split_f16_pair(pr[2 * k], pr[2 * k + 1], dvw[k], hw[k], lw[k]);
+    for (int k = 0; k < 4; ++k) hw[k] = round_f16_pair(pr[2 * k], pr[2 * k + 1], dvw[k]);
     const v8h ahi = __builtin_bit_cast(v8h, hw);
-    const v8h alo = __builtin_bit_cast(v8h, lw);
     if constexpr (VF == 0) {
-      // byte = nibble(dim 32b + col) | nibble(dim 32b + 16 + col) << 4, 8 tokens
+      // byte = nibble(dim 32b + col) | nibble(dim 32b + 16 + col) << 4, 8
+      // tokens; the high nibble is used in place, as 16 * (n - 8) (exact), and
+      // the factor 16 is taken out of those accumulators at the end
       const int R = 16 * b + col;
       const uint2 w = *reinterpret_cast<const uint2*>(
           slot + S::V_OFF + (R * 2 + ((grp >> 1) ^ ((R >> 2) & 1))) * 16 + 8 * (grp & 1));
       const v8h blo = bytes_to_f16x8(w.x & 0x0F0F0F0Fu, w.y & 0x0F0F0F0Fu, (_Float16)1032.0f);
-      const v8h bhi =
-          bytes_to_f16x8((w.x >> 4) & 0x0F0F0F0Fu, (w.y >> 4) & 0x0F0F0F0Fu, (_Float16)1032.0f);
+      const v8h bhi = bytes_to_f16x8(w.x & 0xF0F0F0F0u, w.y & 0xF0F0F0F0u, (_Float16)1152.0f);
       acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, blo, acc[2 * b], 0, 0, 0);
-      acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, blo, acc[2 * b], 0, 0, 0);
       acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bhi, acc[2 * b + 1], 0, 0, 0);
-      acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bhi, acc[2 * b + 1], 0, 0, 0);
     } else {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -1020,7 +1007,6 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
         // int8 code c -> byte c ^ 0x80 = c + 128 -> fp16 (1024 + c + 128) - 1152
         const v8h bv = bytes_to_f16x8(w.x ^ 0x80808080u, w.y ^ 0x80808080u, (_Float16)1152.0f);
         acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bv, acc[n], 0, 0, 0);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bv, acc[n], 0, 0, 0);
       }
     }
   }
@@ -1111,9 +1097,12 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   for (int i = 0; i < 4; ++i) st.lrow[i] = sum_row16(st.lrow[i]);
   __syncthreads();   // every wave is done with its ring
 #pragma unroll
-  for (int n = 0; n < NT; ++n)
+  for (int n = 0; n < NT; ++n) {
+    // q4_0: the high-nibble dims (odd n) accumulated 16 x their value
+    const float sc = (VF == 0 && (n & 1)) ? 0.0625f : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_buf[(wave * kRows + 4 * grp + i) * D + 16 * n + col] = st.acc[n][i];
+    for (int i = 0; i < 4; ++i) s_buf[(wave * kRows + 4 * grp + i) * D + 16 * n + col] = st.acc[n][i] * sc;
+  }
   if (col == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1258,7 +1247,7 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
   }
   uint32_t hw[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) round_f16_pair(pj[2 * k], pj[2 * k + 1], dv[k], hw[k]);
+  for (int k = 0; k < 4; ++k) hw[k] = round_f16_pair(pj[2 * k], pj[2 * k + 1], dv[k]);
   const v8h bpv = __builtin_bit_cast(v8h, hw);
 
   // ---- (P.V)^T: A = V codes of dims 16g + col, tokens 8*grp .. +8
