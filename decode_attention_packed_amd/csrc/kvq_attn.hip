@@ -112,6 +112,7 @@ struct AttnParams {
   int n_seq_groups;       // n_seq * n_kv_heads
   int xcd_local;          // all splits of a group on one XCD (see block_coords)
   int n_groups_pad;       // groups in the grid: n_seq_groups, rounded up to 8 when xcd_local
+  int lpt_seqs;           // > 0: unsplit batch of that many sequences, groups dealt by length
 };
 
 // Chunks from which single calls run the 12-wave build (12 waves x 4 tiles).
@@ -153,6 +154,7 @@ struct BlockCoords {
   int seq, kvh, split;
   bool pad;       // a padding work-group: returns at once
   bool off_xcd;   // this work-group does not sit on the XCD its group expects
+  int len;        // the sequence's length when block_coords read it, else -1
 };
 __device__ __forceinline__ BlockCoords block_coords(const AttnParams& p, int b) {
   int g, split;
@@ -164,6 +166,27 @@ __device__ __forceinline__ BlockCoords block_coords(const AttnParams& p, int b) 
     g = b / p.n_split;
     split = b % p.n_split;
   }
+  int len = -1;
+  if (p.lpt_seqs > 0) {
+    // Unsplit batches: work-group b < N/2 takes the b-th longest group and
+    // work-group N/2 + b the b-th shortest, so the two work-groups that
+    // share a CU carry about the same total.  Every work-group ranks the
+    // sequences by length (longest first, ties by index) itself.
+    const int N = p.n_seq_groups, half = (N + 1) / 2;
+    const int idx = b < half ? b : N - 1 - (b - half);
+    const int lane = __lane_id();
+    const int n = p.lpt_seqs;
+    const int my = lane < n ? p.seq_len[lane] : -1;
+    int rank = 0;
+    for (int j = 0; j < n; ++j) {
+      const int lj = __builtin_amdgcn_readlane(my, j);
+      rank += (lj > my) || (lj == my && j < lane);
+    }
+    const unsigned long long hit = __ballot(lane < n && rank == idx / p.n_kv_heads);
+    const int s = __builtin_amdgcn_readfirstlane((int)__builtin_ctzll(hit));
+    g = __builtin_amdgcn_readfirstlane(s * p.n_kv_heads + idx % p.n_kv_heads);
+    len = __builtin_amdgcn_readlane(my, s);
+  }
   unsigned xcc;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
   BlockCoords c;
@@ -172,6 +195,7 @@ __device__ __forceinline__ BlockCoords block_coords(const AttnParams& p, int b) 
   c.kvh = c.pad ? 0 : g - c.seq * p.n_kv_heads;
   c.split = split;
   c.off_xcd = !p.xcd_local || (int)(xcc & 0xF) != b % kXcds;
+  c.len = len;
   return c;
 }
 
@@ -1037,7 +1061,7 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   const BlockCoords bc = block_coords(p, blk);
   if (bc.pad) return;
   const int split = bc.split, kvh = bc.kvh, seq = bc.seq;
-  const int L = p.seq_len[seq];
+  const int L = bc.len >= 0 ? bc.len : load_uniform(p.seq_len + seq);
   const int n_split_seq = min((L + p.chunk - 1) / p.chunk, p.n_split);   // clamp: see k_split_merge
   if (split >= n_split_seq) return;
   const int c0 = split * p.chunk;
@@ -1300,7 +1324,7 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   const BlockCoords bc = block_coords(p, blk);
   if (bc.pad) return;
   const int split = bc.split, kvh = bc.kvh, seq = bc.seq;
-  const int L = p.seq_len[seq];
+  const int L = bc.len >= 0 ? bc.len : load_uniform(p.seq_len + seq);
   const int n_split_seq = min((L + p.chunk - 1) / p.chunk, p.n_split);   // clamp: see k_split_merge
   if (split >= n_split_seq) return;
   const int c0 = split * p.chunk;
@@ -1535,6 +1559,9 @@ static AttnParams make_params(const kvq_cache& c, const float* q, float* out, in
   p.xcd_local = p.n_seq_groups % kXcds == 0 || (long long)p.n_seq_groups * plan.n_split <= 64;
   p.n_groups_pad = p.xcd_local ? (p.n_seq_groups + kXcds - 1) / kXcds * kXcds : p.n_seq_groups;
   p.merge_launch = 0;
+  // unsplit batches of up to 64 sequences (one lane per sequence when the
+  // work-groups rank them; see block_coords): ragged batch 85.5 -> 75.7 us
+  p.lpt_seqs = (plan.n_split == 1 && n_seq >= 2 && n_seq <= 64 && p.n_groups_pad == p.n_seq_groups) ? n_seq : 0;
   return p;
 }
 

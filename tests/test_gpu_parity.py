@@ -158,6 +158,30 @@ def test_attention_parity(name):
         H.assert_close(got, ref, ci.spec.name)
 
 
+@pytest.mark.parametrize("n_seq,hkv,fmt", [(40, 8, W.V_Q8_0), (23, 15, W.V_Q4_0), (70, 4, W.V_Q4_0)])
+def test_attention_wide_batch_length_order(n_seq, hkv, fmt):
+    """Wide unsplit batches: up to 64 sequences, work-groups take groups in
+    order of decreasing length (first half) and increasing length (second
+    half), each work-group ranking the sequences itself; ties keep sequence
+    order.  Lengths with repeats, an odd group count (23 x 15 = 345) and a
+    batch past 64 sequences (plain order) must all match the oracle."""
+    rng = np.random.default_rng(n_seq * 100 + hkv)
+    D, G = 128, 2
+    lens = rng.integers(1, 700, size=n_seq).astype(np.int32)
+    lens[::5] = lens[0]            # ties
+    lens[1] = 1
+    seg = (int(lens.max()) + 63) // 64 * 64
+    spec = W.CacheSpec("wide", n_seq, 1, G * hkv, hkv, D, int(lens.max()), fmt)
+    ci = W.CacheInputs(spec, rng.standard_normal((n_seq, 1, G * hkv, D)).astype(np.float32),
+                       [rng.standard_normal((int(n), hkv, D)).astype(np.float32) for n in lens],
+                       [rng.standard_normal((int(n), hkv, D)).astype(np.float32) for n in lens],
+                       lens, None, n_seq, seg)
+    _say(f"wide batch {n_seq} seqs x {hkv} kv heads")
+    cache, table, max_segs = H.build_cache(ci)
+    got = H.run_attention(cache, ci, table, max_segs)
+    H.assert_close(got, H.oracle_attention(ci), f"wide batch {n_seq}x{hkv}")
+
+
 @pytest.mark.parametrize("chunk", [1024, 4096])
 def test_attention_ragged_forced_splits(chunk, monkeypatch):
     """The ragged batch with the split size forced small, so its long
