@@ -382,15 +382,13 @@ __device__ __forceinline__ void wait_tiles(int pending) {
   }
 }
 
-// How a work-group's tiles reach its waves.  Every wave starts with tiles w
-// and w + kWaves.  Static dealing continues round-robin (w + 2 kWaves, ...):
-// each wave accumulates the same tiles in the same order on every run, so
-// the output is bit-for-bit reproducible.  Dynamic dealing hands out the
-// rest from an LDS counter, so a wave that runs ahead takes more tiles; the
-// output then varies in its last bits from run to run (which tiles share a
-// wave's running maximum changes the rounding of the P.V operand).  The
-// head_dim-128 column kernels deal statically (measured no slower); the row
-// layout and the head_dim-64 kernels dynamically (faster there).
+// Tiles of a work-group's chunk are dealt to its waves round-robin: wave w
+// takes tiles w, w + kWaves, w + 2 kWaves, ...  Every wave accumulates the
+// same tiles in the same order on every run, so for a fixed split plan the
+// output is bit-for-bit reproducible.  (Handing tiles out from an LDS counter
+// let a wave that runs ahead take more, 1-2 us faster on the verify step,
+// but then which tiles share a wave's running maximum, and with it the fp16
+// rounding of the P.V operand, changed from run to run.)
 constexpr int kWaveStride = kTile * kWaves;
 
 // A wave's tiles in flight: `cur` is the next one to process, `n1` was
@@ -401,40 +399,23 @@ struct TileQueue {
 };
 __device__ __forceinline__ TileQueue first_tiles(int c0, int wave) {
   const int t = c0 + kTile * wave;
-  return {t, t + kWaveStride, 0};
+  return {t, t + kWaveStride, t + 2 * kWaveStride};
 }
-template <bool DYN>
-struct TileDealer {
-  int* s_next;   // dynamic: the LDS counter of the next tile index (starts at 2 kWaves)
-  int c0;
-  // the tile after `prev` (the wave's last dealt tile); uniform across the wave
-  __device__ __forceinline__ int next(int prev) const {
-    if constexpr (!DYN) {
-      return prev + kWaveStride;
-    } else {
-      int i = 0;
-      if (__lane_id() == 0)
-        i = __hip_atomic_fetch_add(s_next, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-      return c0 + kTile * __builtin_amdgcn_readfirstlane(i);
-    }
-  }
-};
 
 // One step of a wave's ring: refill and wait as the slot count allows, then
 // run `body` on the tile in slot SLOT (a compile-time slot, so LDS offsets
 // become immediates).  Returns false once the wave's tiles are done.
-template <int D, int VF, int SLOT, class Dealer, class Body>
+template <int D, int VF, int SLOT, class Body>
 __device__ __forceinline__ bool ring_step(const AttnParams& p, int seq, int kvh, int c1,
                                           uint32_t ring_lds, const TileLane<D, VF>& tl,
-                                          TileCursor& cur, TileQueue& q, const Dealer& deal,
-                                          Body& body) {
+                                          TileCursor& cur, TileQueue& q, Body& body) {
   using S = Slot<D, VF>;
   if (q.cur >= c1) return false;
   if constexpr (S::NSLOT == 3) {
     // the next tile goes into the slot freed last step
     const int n2 = q.g;
     if (n2 < c1) issue_tile<D, VF>(p, seq, kvh, n2, ring_lds + ((SLOT + 2) % 3) * S::BYTES, tl, cur);
-    q.g = deal.next(n2);
+    q.g = n2 + kWaveStride;
     wait_tiles<S::LPT>((q.n1 < c1) + (n2 < c1));
     body(std::integral_constant<int, SLOT>{}, q.cur);
     q.cur = q.n1;
@@ -445,26 +426,25 @@ __device__ __forceinline__ bool ring_step(const AttnParams& p, int seq, int kvh,
     if (q.g < c1) issue_tile<D, VF>(p, seq, kvh, q.g, ring_lds + SLOT * S::BYTES, tl, cur);
     q.cur = q.n1;
     q.n1 = q.g;
-    q.g = deal.next(q.g);
+    q.g += kWaveStride;
   }
   return true;
 }
 
 // Run a wave's ring to the end.  On entry tile q.cur sits in slot 0 and
-// q.n1 in slot 1 (both issued or past the end), and q.g is dealt.
-template <int D, int VF, class Dealer, class Body>
+// q.n1 in slot 1 (both issued or past the end).
+template <int D, int VF, class Body>
 __device__ __forceinline__ void run_ring(const AttnParams& p, int seq, int kvh, int c1,
                                          uint32_t ring_lds, const TileLane<D, VF>& tl,
-                                         TileCursor& cur, TileQueue& q, const Dealer& deal,
-                                         Body& body) {
+                                         TileCursor& cur, TileQueue& q, Body& body) {
   if constexpr (Slot<D, VF>::NSLOT == 3) {
-    while (ring_step<D, VF, 0>(p, seq, kvh, c1, ring_lds, tl, cur, q, deal, body) &&
-           ring_step<D, VF, 1>(p, seq, kvh, c1, ring_lds, tl, cur, q, deal, body) &&
-           ring_step<D, VF, 2>(p, seq, kvh, c1, ring_lds, tl, cur, q, deal, body)) {
+    while (ring_step<D, VF, 0>(p, seq, kvh, c1, ring_lds, tl, cur, q, body) &&
+           ring_step<D, VF, 1>(p, seq, kvh, c1, ring_lds, tl, cur, q, body) &&
+           ring_step<D, VF, 2>(p, seq, kvh, c1, ring_lds, tl, cur, q, body)) {
     }
   } else {
-    while (ring_step<D, VF, 0>(p, seq, kvh, c1, ring_lds, tl, cur, q, deal, body) &&
-           ring_step<D, VF, 1>(p, seq, kvh, c1, ring_lds, tl, cur, q, deal, body)) {
+    while (ring_step<D, VF, 0>(p, seq, kvh, c1, ring_lds, tl, cur, q, body) &&
+           ring_step<D, VF, 1>(p, seq, kvh, c1, ring_lds, tl, cur, q, body)) {
     }
   }
 }
@@ -1041,7 +1021,6 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
 
 template <int D, int VF>
 __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
-  constexpr bool kDynamicTiles = true;
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
   constexpr int NT = D / 16;
@@ -1052,7 +1031,6 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
 
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   __shared__ int s_last;
-  __shared__ int s_next;   // the dynamic dealer's next tile index
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1071,8 +1049,6 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   TileCursor cur = {-1, 0};
   TileQueue tq = first_tiles(c0, wave);
   const uint32_t ring_lds = lds_addr(s_lds + wave * S::NSLOT * S::BYTES);
-  const TileDealer<kDynamicTiles> deal = {&s_next, c0};
-  if (kDynamicTiles && tid == 0) s_next = 2 * kWaves;
 
   int8_t* s_qc;
   float* s_qd;
@@ -1093,7 +1069,6 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   }
   __syncthreads();   // every wave has its operands; wave 0's last slot is free
   if (S::NSLOT == 2 && tq.n1 < c1) issue_tile<D, VF>(p, seq, kvh, tq.n1, ring_lds + S::BYTES, tl, cur);
-  tq.g = deal.next(tq.n1);
 
   WaveState<D> st;
 #pragma unroll
@@ -1110,7 +1085,7 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
     if (t0 + kTile > app.lo && t0 < app.hi) patch_tile<D, VF>(ring + SL * S::BYTES, s_patch, t0, app);
     process_tile<D, VF>(ring + SL * S::BYTES, pbuf, t0, c1, qa, dqs, vis, st);
   };
-  run_ring<D, VF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, deal, body);
+  run_ring<D, VF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
   if (app.hi > app.lo) write_appended<D, VF>(p, seq, kvh, app, s_patch);
 
   // ---- this wave's rows to LDS for the merge
@@ -1304,7 +1279,6 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
 
 template <int D, int VF>
 __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
-  constexpr bool kDynamicTiles = D != 128;
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
   constexpr int NG = D / 16;
@@ -1315,7 +1289,6 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
 
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   __shared__ int s_last;
-  __shared__ int s_next;   // the dynamic dealer's next tile index
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1334,8 +1307,6 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   TileCursor cur = {-1, 0};
   TileQueue tq = first_tiles(c0, wave);
   const uint32_t ring_lds = lds_addr(s_lds + wave * S::NSLOT * S::BYTES);
-  const TileDealer<kDynamicTiles> deal = {&s_next, c0};
-  if (kDynamicTiles && tid == 0) s_next = 2 * kWaves;
 
   int8_t* s_qc;
   float* s_qd;
@@ -1365,7 +1336,6 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   const int vis_min = min(p.causal ? L - p.n_qtok + 1 : L, c1);   // the first query token's
   __syncthreads();   // every wave has its operands; wave 0's last slot is free
   if (S::NSLOT == 2 && tq.n1 < c1) issue_tile<D, VF>(p, seq, kvh, tq.n1, ring_lds + S::BYTES, tl, cur);
-  tq.g = deal.next(tq.n1);
 
   ColState<D> st;
 #pragma unroll
@@ -1383,7 +1353,7 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
                              qb, wq, st);
     first = false;
   };
-  run_ring<D, VF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, deal, body);
+  run_ring<D, VF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
   if (app.hi > app.lo) write_appended<D, VF>(p, seq, kvh, app, s_patch);
 
   // ---- this wave's rows to LDS for the merge
