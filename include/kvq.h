@@ -145,9 +145,16 @@ int attn_decode_packed_workspace_size(const kvq_cache* cache, int n_seq, int n_q
  * int8 per 32-block with an fp32 scale (a = max|q|, d = a/127, codes as for K),
  * QK^T is summed in int32 per block and rescaled in fp32, softmax runs per
  * context split with an online maximum, V is dequantized inside the
- * weighted sum, and the last work-group of each (sequence, kv head) merges
- * the splits.  n_qtok * (n_q_heads / n_kv_heads) must be at most 16
- * (KVQ_ERR_UNSUPPORTED otherwise).
+ * weighted sum (each weight p times the V block scale rounded once to fp16,
+ * the sum kept in fp32), and the splits are merged by the last work-group of
+ * each (sequence, kv head), or, for more than 4 query rows per kv head at
+ * head_dim 128 (8 at 64), by a second launch on the same stream.
+ * n_qtok * (n_q_heads / n_kv_heads) must be at most 16 (KVQ_ERR_UNSUPPORTED
+ * otherwise).  The split plan depends only on the shape arguments (n_seq,
+ * n_qtok, n_q_heads, max_seq_len and the cache geometry; the environment
+ * variable KVQ_CHUNK_TOKENS, a multiple of 256, overrides its split size for
+ * tests); for a given plan the output bits are a pure function of the
+ * inputs, identical from call to call.
  */
 int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n_seq,
                        int n_qtok, int n_q_heads, const int32_t* seg_table, int max_segs,
