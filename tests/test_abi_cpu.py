@@ -102,6 +102,44 @@ def test_workspace_size_is_host_only():
                                                       ctypes.byref(out)) == K.KVQ_ERR_INVALID
 
 
+def _r256(x):
+    return (x + 255) // 256 * 256
+
+
+def _splits_from_workspace(c, n_seq, n_qtok, hq, max_len):
+    """The split count the planner chose, read back from the workspace size
+    (counters, then [groups][splits][rows][D] partial rows, then their (m, l))."""
+    out = ctypes.c_size_t(0)
+    assert K.lib().attn_decode_packed_workspace_size(ctypes.byref(c), n_seq, n_qtok, hq, max_len,
+                                                      ctypes.byref(out)) == 0
+    groups = n_seq * c.n_kv_heads
+    rows = n_qtok * (hq // c.n_kv_heads)
+    hits = [s for s in range(1, 65)
+            if _r256(groups * 4) + _r256(groups * s * rows * c.head_dim * 4) + _r256(groups * s * rows * 8)
+            == out.value]
+    assert len(hits) == 1, (out.value, hits)
+    return hits[0]
+
+
+@pytest.mark.parametrize("hkv,d,n_seq,hq,max_len,want", [
+    (1, 128, 1, 4, 512, 1),         # short sequence, few groups: one split, no merge
+    (1, 128, 1, 4, 1024, 4),        # from 1024 tokens: 256-token splits
+    (8, 128, 1, 32, 8192, 32),      # gqa8k: about 256 work-groups
+    (8, 128, 1, 32, 131072, 32),    # the 128k step: 4096-token chunks
+    (32, 64, 16, 32, 32768, 1),     # ragged: 512 groups, unsplit
+    (16, 128, 16, 32, 32768, 2),    # 256 groups: the longest sequence in two
+    (4, 128, 75, 8, 4096, 1),       # 300 groups: unsplit
+])
+def test_split_plan(hkv, d, n_seq, hq, max_len, want):
+    """The split planner's rules, pinned through the workspace size (host
+    only): about one work-group per CU for few groups with at least 8 splits
+    per sequence, no split for sequences of at most 512 tokens, and at most
+    two (sequence, kv head) groups' worth of work-groups per CU for wide
+    batches."""
+    c = _fake_cache(n_kv_heads=hkv, head_dim=d, seg_tokens=max_len)
+    assert _splits_from_workspace(c, n_seq, 1, hq, max_len) == want
+
+
 def test_bad_append_args_rejected():
     c = _fake_cache()
     L = K.lib()
