@@ -79,3 +79,26 @@ def test_batch_column_layout_mixed_shapes():
         H.assert_close(got, H.oracle_attention(ci), "batch cols " + ci.spec.name)
     # each call's counters (the first bytes of its workspace part) end at zero
     assert not ws.cpu().numpy()[:16].any()
+
+
+def test_batch_wide_unsplit_call_with_split_call():
+    """A wide unsplit call (24 sequences x 16 kv heads, lengths with ties:
+    its work-groups take groups by length) and a split call (8 kv heads, 32
+    splits merged in their last work-group) in one launch; each must match
+    the oracle and leave its counters at zero."""
+    rng = np.random.default_rng(5151)
+    S, hkv, G, D = 24, 16, 2, 128
+    lens = rng.integers(1, 900, size=S).astype(np.int32)
+    lens[::4] = lens[1]
+    seg = (int(lens.max()) + 63) // 64 * 64
+    spec = W.CacheSpec("wide", S, 1, G * hkv, hkv, D, int(lens.max()), W.V_Q4_0)
+    wide = W.CacheInputs(spec, rng.standard_normal((S, 1, G * hkv, D)).astype(np.float32),
+                         [rng.standard_normal((int(n), hkv, D)).astype(np.float32) for n in lens],
+                         [rng.standard_normal((int(n), hkv, D)).astype(np.float32) for n in lens],
+                         lens, None, S, seg)
+    cis = [wide, W.make_inputs("gqa8k", ctx=4096)[0]]
+    _say("batch wide unsplit + split")
+    outs, ws = run_batch(cis)
+    for ci, got in zip(cis, outs):
+        H.assert_close(got, H.oracle_attention(ci), "batch " + ci.spec.name)
+    assert not ws.cpu().numpy()[:4 * S * hkv].any()
