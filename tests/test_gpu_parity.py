@@ -232,12 +232,16 @@ def test_attention_shapes_and_ragged_tails(D, G, fmt, L):
     H.assert_close(got, H.oracle_attention(ci), f"D{D} G{G} f{fmt} L{L}")
 
 
-@pytest.mark.parametrize("Tq,G,causal,L,fmt", [(4, 4, True, 2000, 0), (2, 8, True, 333, 1),
-                                              (16, 1, True, 130, 0), (3, 4, False, 4100, 1),
-                                              (4, 2, True, 4, 0), (5, 3, True, 700, 1)])
-def test_attention_multi_query(Tq, G, causal, L, fmt):
-    rng = np.random.default_rng(Tq * 100 + G * 10 + L)
-    Hkv, D = 2, 128
+@pytest.mark.parametrize("D,Tq,G,causal,L,fmt", [(128, 4, 4, True, 2000, 0), (128, 2, 8, True, 333, 1),
+                                                (128, 16, 1, True, 130, 0), (128, 3, 4, False, 4100, 1),
+                                                (128, 4, 2, True, 4, 0), (128, 5, 3, True, 700, 1),
+                                                (64, 4, 4, True, 1500, 1), (64, 16, 1, True, 300, 0),
+                                                (64, 3, 4, False, 2100, 0), (64, 9, 1, True, 9, 1)])
+def test_attention_multi_query(D, Tq, G, causal, L, fmt):
+    """The row layout (more than 16 query-row x block columns): head_dim 128
+    and 64, both V formats, causal and not, contexts down to the query count."""
+    rng = np.random.default_rng(D * 7 + Tq * 100 + G * 10 + L)
+    Hkv = 2
     spec = W.CacheSpec("mq", 1, Tq, G * Hkv, Hkv, D, L, fmt, causal=causal)
     cap = -(-L // 64) * 64
     ci = W.CacheInputs(spec, rng.standard_normal((1, Tq, G * Hkv, D)).astype(np.float32),
@@ -246,7 +250,7 @@ def test_attention_multi_query(Tq, G, causal, L, fmt):
                        np.array([L], np.int32), None, 1, cap)
     cache, table, max_segs = H.build_cache(ci)
     got = H.run_attention(cache, ci, table, max_segs)
-    H.assert_close(got, H.oracle_attention(ci), f"Tq{Tq} G{G} causal{causal} L{L}")
+    H.assert_close(got, H.oracle_attention(ci), f"D{D} Tq{Tq} G{G} causal{causal} L{L}")
 
 
 @pytest.mark.parametrize("D,Tq,G,L,fmt", [(128, 2, 2, 517, 0), (128, 4, 1, 1000, 1),
