@@ -104,7 +104,7 @@ struct AttnParams {
   int rows;               // n_qtok * group, at most 16
   int seg_tokens;
   int max_segs;
-  int chunk;              // tokens per work-group, a multiple of kWaves * kTile
+  int chunk;              // tokens per work-group, a multiple of kTile
   int n_split;
   int causal;
   float scale_log2;       // sm_scale * log2(e)

@@ -26,6 +26,7 @@ struct WorkspaceLayout {
   size_t total;
 };
 
+constexpr int kTileTokens = 32;    // tokens per tile: split points fall on tile boundaries
 constexpr int kChunkAlign = 256;   // one 32-token tile for each of the 8 waves of a work-group
 constexpr int kMaxSplits = 64;     // splits per (sequence, kv head) the merge stages in LDS
 
