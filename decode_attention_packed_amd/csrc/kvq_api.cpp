@@ -88,8 +88,17 @@ SplitPlan plan_splits(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads, 
       // kv heads: 7.9 us against 9.3 us in two splits; from 1024 tokens
       // 256-token splits are faster again).
       chunk = 2 * kChunkAlign;
+    } else if (n_groups * 8 <= target_groups) {
+      // Few groups (at most 32): 256 / groups splits per sequence (at most
+      // kMaxSplits), each a whole number of tiles, so one work-group per CU
+      // carries a near-equal share at any length.  Power-of-two chunks gave
+      // 33 splits at 131073 tokens: 8 one-token work-groups in a second
+      // round after the rest of the grid.
+      const long long want = std::min<long long>(target_groups / n_groups, kMaxSplits);
+      const long long per = (max_seq_len + want - 1) / want;
+      chunk = (int)std::max<long long>(kChunkAlign, (per + kTileTokens - 1) / kTileTokens * kTileTokens);
     } else {
-      // Few groups: grow the chunk while at least one work-group per CU
+      // Up to 255 groups: grow the chunk while at least one work-group per CU
       // remains and the longest sequence still spreads over 8 or more.
       while (chunk < (1 << 20)) {
         const long long next = 2LL * chunk;

@@ -126,6 +126,10 @@ def _splits_from_workspace(c, n_seq, n_qtok, hq, max_len):
     (1, 128, 1, 4, 1024, 4),        # from 1024 tokens: 256-token splits
     (8, 128, 1, 32, 8192, 32),      # gqa8k: about 256 work-groups
     (8, 128, 1, 32, 131072, 32),    # the 128k step: 4096-token chunks
+    (8, 128, 1, 32, 131073, 32),    # one token more: still 32 splits (4128 tokens), not 33
+    (8, 128, 1, 32, 100000, 32),    # any length: one work-group per CU
+    (4, 128, 1, 16, 131072, 64),    # the verify step's draft cache alone
+    (16, 128, 2, 32, 50000, 8),     # 32 groups: 8 splits
     (32, 64, 16, 32, 32768, 1),     # ragged: 512 groups, unsplit
     (16, 128, 16, 32, 32768, 2),    # 256 groups: the longest sequence in two
     (4, 128, 75, 8, 4096, 1),       # 300 groups: unsplit
@@ -136,7 +140,7 @@ def test_split_plan(hkv, d, n_seq, hq, max_len, want):
     per sequence, no split for sequences of at most 512 tokens, and at most
     two (sequence, kv head) groups' worth of work-groups per CU for wide
     batches."""
-    c = _fake_cache(n_kv_heads=hkv, head_dim=d, seg_tokens=max_len)
+    c = _fake_cache(n_kv_heads=hkv, head_dim=d, seg_tokens=(max_len + 63) // 64 * 64)
     assert _splits_from_workspace(c, n_seq, 1, hq, max_len) == want
 
 
