@@ -60,6 +60,13 @@ int check_attn(const kvq_cache* c, const float* q, const float* out, int n_seq, 
 
 namespace kvq {
 
+// The smallest chunk of whole tiles (at least kChunkAlign tokens) that
+// covers `len` tokens in `n` splits.
+static int even_chunk(long long len, long long n) {
+  const long long per = (len + n - 1) / n;
+  return (int)std::max<long long>(kChunkAlign, (per + kTileTokens - 1) / kTileTokens * kTileTokens);
+}
+
 SplitPlan plan_splits(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads, int max_seq_len) {
   (void)n_qtok;
   (void)n_q_heads;
@@ -82,6 +89,7 @@ SplitPlan plan_splits(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads, 
       // 4096-token chunks).
       const long long most = std::max<long long>(1, 2 * target_groups / n_groups);
       while (chunk < (1 << 20) && splits(chunk) > most) chunk *= 2;
+      chunk = even_chunk(max_seq_len, splits(chunk));
     } else if (splits(2 * kChunkAlign) == 1) {
       // Short sequences (two tiles per wave at most): one work-group per
       // group writes its rows directly, with no split merge (512 tokens, 1-4
@@ -94,9 +102,7 @@ SplitPlan plan_splits(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads, 
       // carries a near-equal share at any length.  Power-of-two chunks gave
       // 33 splits at 131073 tokens: 8 one-token work-groups in a second
       // round after the rest of the grid.
-      const long long want = std::min<long long>(target_groups / n_groups, kMaxSplits);
-      const long long per = (max_seq_len + want - 1) / want;
-      chunk = (int)std::max<long long>(kChunkAlign, (per + kTileTokens - 1) / kTileTokens * kTileTokens);
+      chunk = even_chunk(max_seq_len, std::min<long long>(target_groups / n_groups, kMaxSplits));
     } else {
       // Up to 255 groups: grow the chunk while at least one work-group per CU
       // remains and the longest sequence still spreads over 8 or more.
@@ -105,6 +111,9 @@ SplitPlan plan_splits(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads, 
         if (n_groups * splits(next) < target_groups || splits(next) < 8) break;
         chunk = (int)next;
       }
+      // the nearest split count, in even chunks (just past a power of two
+      // the loop above leaves a near-empty last split: 9 at 131073 tokens)
+      chunk = even_chunk(max_seq_len, std::max<long long>(1, (max_seq_len + chunk / 2) / chunk));
     }
   }
   // the split merge stages at most kMaxSplits partials per (sequence, kv head)

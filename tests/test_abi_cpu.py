@@ -130,6 +130,9 @@ def _splits_from_workspace(c, n_seq, n_qtok, hq, max_len):
     (8, 128, 1, 32, 100000, 32),    # any length: one work-group per CU
     (4, 128, 1, 16, 131072, 64),    # the verify step's draft cache alone
     (16, 128, 2, 32, 50000, 8),     # 32 groups: 8 splits
+    (8, 128, 8, 32, 131072, 8),     # 64 groups: at least 8 splits per sequence
+    (8, 128, 8, 32, 131073, 8),     # one token more: still 8 (even chunks), not 9
+    (16, 128, 16, 32, 32769, 2),    # 256 groups one token past 32k: two even splits
     (32, 64, 16, 32, 32768, 1),     # ragged: 512 groups, unsplit
     (16, 128, 16, 32, 32768, 2),    # 256 groups: the longest sequence in two
     (4, 128, 75, 8, 4096, 1),       # 300 groups: unsplit
