@@ -239,8 +239,9 @@ int check_call(const kvq_attn_call* a, kvq::AttnCall* out) {
 // Validate a batch; on success fills calls[], plans[] and the workspace size.
 // One launch runs every call, so the split plan is joint: with fewer than
 // 256 (sequence, kv head) groups in all, one chunk length for every call,
-// the shortest multiple of 256 tokens that keeps the whole grid within one
-// work-group per CU; otherwise each call's own plan.
+// the shortest whole number of 32-token tiles (at least 256 tokens) that
+// keeps the whole grid within one work-group per CU; otherwise each call's
+// own plan.
 int check_batch(const kvq_attn_call* calls, int n_calls, kvq::AttnCall* out, kvq::SplitPlan* plans,
                 size_t* ws_bytes) {
   if (!calls || n_calls < 1 || n_calls > KVQ_MAX_BATCH) return KVQ_ERR_INVALID;

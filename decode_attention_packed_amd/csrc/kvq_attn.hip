@@ -1,15 +1,15 @@
 // Split-K decode attention over the packed cache (MFMA path).
 //
-// One work-group of eight waves (one per CU) owns one (sequence, kv head,
-// context chunk) and all query rows of that kv group (query tokens x query
-// heads, at most 16), so grouped query heads and the verify step's query
-// tokens share every K/V byte loaded.  The chunk's 32-token tiles are handed
-// out to the waves in order from an LDS counter, so waves that run ahead take
-// more of them.
+// One work-group of eight waves (twelve in the w12 build below; one
+// work-group per CU) owns one (sequence, kv head, context chunk) and all
+// query rows of that kv group (query tokens x query heads, at most 16), so
+// grouped query heads and the verify step's query tokens share every K/V
+// byte loaded.  The chunk's 32-token tiles are dealt to the waves
+// round-robin, so every run accumulates the same tiles in the same order.
 //
 // Memory: each wave streams its tiles through a ring of LDS slots with
 // direct global->LDS loads (16 bytes per lane), up to two tiles ahead of the
-// one it is working on, so a CU keeps ~130 KB of K/V in flight without
+// one it is working on, so a CU keeps 100-160 KB of K/V in flight without
 // holding it in registers.  K rows are XOR-swizzled on their way into LDS so
 // the 8-byte operand reads spread over the banks.
 //
@@ -39,10 +39,11 @@
 // rows are query rows; the per-block dots come from one MFMA per block, P
 // goes through LDS into the A operand and B is the dequantized V.
 //
-// The eight waves merge through LDS and the group writes one unnormalized
-// partial (m, l, o) per row.  The last group to finish a (sequence, kv head)
-// -- counted with a device-scope atomic in the workspace -- merges all of
-// its partials and writes the output rows, then resets the counter.
+// The waves merge through LDS and the work-group writes one unnormalized
+// partial (m, l, o) per row.  Column layout: the last work-group to finish a
+// (sequence, kv head) -- counted with a device-scope atomic in the workspace
+// -- merges all of its partials and writes the output rows, then resets the
+// counter.  Row layout: a second launch (k_split_merge) merges them.
 
 #include "kvq_device.h"
 #include "kvq_launch.h"
