@@ -137,6 +137,8 @@ int attn_decode_packed_workspace_size(const kvq_cache* cache, int n_seq, int n_q
  *   out      device float [n_seq][n_qtok][n_q_heads][head_dim]
  *   seq_len  device int32 [n_seq], each in [max(1, n_qtok), max_seq_len]
  *   max_seq_len  host bound on seq_len (sizes the split grid)
+ *   n_seq, n_qtok (at most KVQ_MAX_QTOK), n_q_heads and max_seq_len must be
+ *   at least 1: an empty call is KVQ_ERR_INVALID, not a no-op
  *   sm_scale softmax scale (1/sqrt(head_dim) in the usual model)
  *   causal   if nonzero, query j sits at position seq_len - n_qtok + j and
  *            sees tokens up to and including that position; otherwise every

@@ -90,6 +90,10 @@ def test_bad_attention_args_rejected():
     assert _attn(c, scale=float("nan")) == K.KVQ_ERR_INVALID
     assert _attn(c, ws_bytes=16) == K.KVQ_ERR_WORKSPACE
     assert _attn(c, ws=None) == K.KVQ_ERR_WORKSPACE
+    # empty calls are rejected before any launch, not run as no-ops
+    assert _attn(c, n_seq=0) == K.KVQ_ERR_INVALID
+    assert _attn(c, n_qtok=0) == K.KVQ_ERR_INVALID
+    assert _attn(c, max_len=0) == K.KVQ_ERR_INVALID
 
 
 def test_workspace_size_is_host_only():
