@@ -108,7 +108,8 @@ int kvq_cache_bytes(int n_kv_heads, int head_dim, int seg_tokens, int n_segs,
 /*
  * kv_append_quant: quantize and pack new K/V rows into the cache (page 1:
  * the K payload is re-packed as it is written; V is written as q4_0/q8_0).
- *   k_new, v_new  device float [n_seq][n_new][n_kv_heads][head_dim]
+ *   k_new, v_new  device float [n_seq][n_new][n_kv_heads][head_dim]; n_seq
+ *                 and n_new at least 1 (KVQ_ERR_INVALID otherwise)
  *   start_pos     device int32 [n_seq]; row j of sequence i goes to token
  *                 start_pos[i] + j, which must be < max_segs*seg_tokens and
  *                 must map to a segment < n_segs
