@@ -34,9 +34,15 @@ rescaling.
 
 Pins (tests under tests/ marked "not gpu"): nearest-half brute force over
 all 65536 binary16 values; exact rational arg-min over all codes for the
-quantizers; the round-trip bound; hand-derived worked blocks and the 47%
-closed form under tests/golden/; 50-digit mpmath brute force and softmax
-invariants for the attention.  No function here is parity unpinned.
+quantizers; the round-trip bound, per element against its own block's scale
+on rows whose blocks differ in magnitude by 10-10^6 (head_dim 64 and 128);
+hand-derived worked blocks and the 47% closed form under tests/golden/; a
+50-digit mpmath evaluation of the whole decode step from the raw cache bytes
+at head_dim 32, 64 and 128 (one, two and four blocks per row, block scales an
+order of magnitude apart, four query heads per kv head, causal and not, both
+V formats); softmax invariants for the attention.  A dequantizer that paired
+an element with another block's scale fails both the round-trip and the
+mpmath pins.  No function here is parity unpinned.
 """
 from __future__ import annotations
 

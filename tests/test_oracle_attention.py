@@ -65,33 +65,55 @@ def _mp_attention(q_row, k_rows, v_rows, scale):
     return [mpmath.fsum(e[t] * v_rows[t][c] for t in range(len(e))) / z for c in range(D)]
 
 
+# Per-block magnitudes (factors of 10-100 between blocks) so that every
+# element's dequantized value depends on its own block's scale: an oracle that
+# paired an element with another block's scale would move the scores or the
+# output far outside the tolerance.  Q's factors are the inverse of K's, which
+# keeps every block's share of the score of order one.
+_K_BLOCK_GAIN = {32: [2.0], 64: [0.1, 10.0], 128: [0.1, 2.0, 20.0, 0.5]}
+_V_BLOCK_GAIN = {32: [1.0], 64: [10.0, 0.1], 128: [1.0, 0.05, 8.0, 0.3]}
+
+
+@pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("fmt", [O.V_Q4_0, O.V_Q8_0])
 @pytest.mark.parametrize("causal", [False, True])
-def test_decode_attention_mp_bruteforce(fmt, causal):
-    rng = np.random.default_rng(10 + fmt + 2 * causal)
-    S, Tq, Hq, Hkv, D, Lmax = 2, 2, 4, 2, 32, 8
+def test_decode_attention_mp_bruteforce(D, fmt, causal):
+    """The whole decode step against a 50-digit evaluation written from the
+    raw cache bytes: K words unpacked byte by byte, q4_0 bytes split into
+    their two nibbles, every element times the binary16 scale of its own
+    32-block (page 1: 32-element blocks with one fp16 scale each), Q codes
+    times their fp32 block scale, then the softmax definition.  Four query
+    heads share each kv head (grouped-query attention)."""
+    rng = np.random.default_rng(10 + fmt + 2 * causal + D)
+    S, Tq, Hq, Hkv, Lmax = 2, 2, 8, 2, 8
     seq_len = [8, 5]
-    q = rng.standard_normal((S, Tq, Hq, D)).astype(np.float32)
-    k = (rng.standard_normal((S, Hkv, Lmax, D)) * 2).astype(np.float32)
-    v = rng.standard_normal((S, Hkv, Lmax, D)).astype(np.float32)
+    kg = np.repeat(np.asarray(_K_BLOCK_GAIN[D], np.float32), 32)
+    vg = np.repeat(np.asarray(_V_BLOCK_GAIN[D], np.float32), 32)
+    q = (rng.standard_normal((S, Tq, Hq, D)) / kg).astype(np.float32)
+    k = (rng.standard_normal((S, Hkv, Lmax, D)) * kg).astype(np.float32)
+    v = (rng.standard_normal((S, Hkv, Lmax, D)) * vg).astype(np.float32)
     kw, kd = O.encode_k(k)
     vp, vd = O.encode_v(v, fmt)
+    if D > 32:
+        # the blocks' scales really differ by an order of magnitude or more
+        ks = O.half_value(kd[0, 0, 0]).astype(np.float64)
+        assert ks.max() / ks.min() >= 10
     scale = 1 / math.sqrt(D)
     got = O.decode_attention(q, kw, kd, vp, vd, fmt, seq_len, scale, causal)
     qc, qd = O.quantize_q(q)
     G = Hq // Hkv
     for i in range(S):
         L = seq_len[i]
-        for j in range(Tq):
-            n_vis = L - Tq + j + 1 if causal else L
-            for h in range(Hq):
-                kvh = h // G
-                k_rows = [_k_row_mp(kw[i, kvh, t], kd[i, kvh, t]) for t in range(n_vis)]
-                v_rows = [_v_row_mp(vp[i, kvh, t], vd[i, kvh, t], fmt, D) for t in range(n_vis)]
-                want = _mp_attention(_q_row_mp(qc[i, j, h], qd[i, j, h]), k_rows, v_rows,
-                                     mpmath.mpf(scale))
-                want = np.array([float(x) for x in want])
-                np.testing.assert_allclose(got[i, j, h], want, rtol=1e-12, atol=1e-13)
+        for kvh in range(Hkv):
+            k_rows = [_k_row_mp(kw[i, kvh, t], kd[i, kvh, t]) for t in range(L)]
+            v_rows = [_v_row_mp(vp[i, kvh, t], vd[i, kvh, t], fmt, D) for t in range(L)]
+            for j in range(Tq):
+                n_vis = L - Tq + j + 1 if causal else L
+                for h in range(kvh * G, (kvh + 1) * G):
+                    want = _mp_attention(_q_row_mp(qc[i, j, h], qd[i, j, h]), k_rows[:n_vis],
+                                         v_rows[:n_vis], mpmath.mpf(scale))
+                    want = np.array([float(x) for x in want])
+                    np.testing.assert_allclose(got[i, j, h], want, rtol=1e-12, atol=1e-13)
 
 
 def test_closed_form_two_tokens():

@@ -314,3 +314,48 @@ def test_k_saving_matches_page_figure():
     assert O.kv_bytes_per_token_head(128, O.V_Q4_0) == (136, 72)
     assert O.kv_bytes_per_token_head(128, O.V_Q8_0) == (136, 136)
     assert O.kv_bytes_per_token_head(64, O.V_Q8_0) == (68, 68)
+
+
+# ---------------------------------------------------------------------------
+# dequantization of whole rows: every element takes its own block's scale
+# ---------------------------------------------------------------------------
+
+def _rows_with_block_gains(rng, n, gains):
+    """n rows of len(gains) 32-blocks, block b drawn N(0, 1) times gains[b]."""
+    g = np.repeat(np.asarray(gains, np.float64), 32)
+    return (rng.standard_normal((n, g.size)) * g).astype(np.float32)
+
+
+@pytest.mark.parametrize("gains", [[0.01, 1.0, 100.0, 0.1], [50.0, 0.02], [1.0, 1e-3, 1e3, 7.0]])
+def test_dequant_rows_per_block_roundtrip(gains):
+    """Page 1 fixes 32-element blocks with one fp16 scale each (the 47% of its
+    title); per element, |x - deq(q(x))| <= d_b / 2 with d_b the scale of the
+    element's own block (the q4_0 clamped top code: <= |d_b|).  Blocks whose
+    scales differ by 10-10^6 make any mix-up of blocks fail the bound."""
+    rng = np.random.default_rng(len(gains) * 7 + int(gains[0] * 100))
+    x = _rows_with_block_gains(rng, 64, gains)
+    x64 = x.astype(np.float64)
+    nb = len(gains)
+
+    def per_elem(d):   # [rows][nb] -> [rows][nb * 32]
+        return np.repeat(np.abs(np.asarray(d, np.float64)), 32, axis=-1)
+
+    kw, kd = O.encode_k(x)
+    dk = per_elem(O.half_value(kd))
+    assert np.all(np.abs(x64 - O.dequant_k(kw, kd)) <= dk / 2 * (1 + 2.0 ** -20))
+
+    vp, vd = O.encode_v(x, O.V_Q8_0)
+    assert np.all(np.abs(x64 - O.dequant_v(vp, vd, O.V_Q8_0)) <= per_elem(O.half_value(vd)) / 2 * (1 + 2.0 ** -20))
+
+    n, d4 = O.quantize_v_q4_0(x)
+    dv = per_elem(O.half_value(d4))
+    err = np.abs(x64 - O.dequant_v(O.pack_q4_0(n), d4, O.V_Q4_0))
+    tail = n == 15
+    assert np.all(err[~tail] <= dv[~tail] / 2 * (1 + 2.0 ** -20))
+    assert np.all(err[tail] <= dv[tail] * (1 + 2.0 ** -10))
+
+    qc, qd = O.quantize_q(x)
+    assert np.all(np.abs(x64 - O.dequant_q(qc, qd)) <= per_elem(qd) / 2 * (1 + 2.0 ** -20))
+    # and the scales themselves follow the blocks' magnitudes
+    ratio = O.half_value(kd).astype(np.float64).mean(axis=0)
+    assert np.all(np.diff(np.log10(ratio)) != 0) and ratio.max() / ratio.min() >= 10 ** (nb > 1)
