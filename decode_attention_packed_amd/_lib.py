@@ -32,7 +32,7 @@ EXPORTS = ("kvq_abi_version", "kvq_status_string", "kvq_cache_bytes", "kv_append
            "attn_decode_packed_workspace_size", "attn_decode_packed", "kvq_debug_quant_q",
            "kvq_debug_qk_isum", "kvq_debug_stream_read", "kvq_f16k_cache_bytes", "kv_append_f16k",
            "attn_decode_f16k_workspace_size", "attn_decode_f16k", "attn_decode_packed_batch",
-           "attn_decode_packed_batch_workspace_size")
+           "attn_decode_packed_batch_workspace_size", "kvq_debug_attn_isum")
 
 
 class KvqCacheStruct(ctypes.Structure):
@@ -107,6 +107,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_debug_qk_isum.restype = c_int
         L.kvq_debug_qk_isum.argtypes = [P, c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_void_p,
                                         c_int, c_void_p, c_void_p]
+        L.kvq_debug_attn_isum.restype = c_int
+        L.kvq_debug_attn_isum.argtypes = L.attn_decode_packed.argtypes[:-1] + [c_void_p, c_void_p]
         if L.kvq_abi_version() != 1:
             raise ImportError("libkvq ABI version mismatch")
         _lib = L
@@ -378,7 +380,7 @@ def attn_decode_packed_batch_workspace_size(calls) -> int:
     arr = _batch_calls(calls)
     out = c_size_t(0)
     _check(lib().attn_decode_packed_batch_workspace_size(arr, len(calls), ctypes.byref(out)),
-           "attn_decode_packed_batch_workspace_size")
+           "attn_decode_packed_batch_workspace_size", "kvq_debug_attn_isum")
     return int(out.value)
 
 
@@ -426,3 +428,18 @@ def kvq_debug_qk_isum(cache: PackedKVCache, q, seq_len, max_seq_len: int, isum, 
     _check(lib().kvq_debug_qk_isum(ctypes.byref(cache.struct), _ptr(q), n_seq, n_qtok, n_q_heads,
                                    _ptr(seg_table), int(max_segs), _ptr(seq_len), int(max_seq_len),
                                    _ptr(isum), _stream(stream)), "kvq_debug_qk_isum")
+
+
+def kvq_debug_attn_isum(cache: PackedKVCache, q, out, seq_len, max_seq_len: int, sm_scale: float,
+                        causal: bool, workspace, isum, seg_table=None, max_segs: int | None = None,
+                        stream=None) -> None:
+    """attn_decode_packed that also stores the kernels' per-block int32 Q.K
+    sums: isum int32 [n_seq][n_qtok][n_q_heads][max_seq_len][D/32]."""
+    import torch
+    _need(isum, torch.int32, "isum", 5)
+    fn = lib().kvq_debug_attn_isum
+
+    def call(*args):
+        return fn(*args[:-1], _ptr(isum), args[-1])
+    _attend(call, "kvq_debug_attn_isum", cache, q, out, seq_len, max_seq_len, sm_scale, causal,
+            workspace, seg_table, max_segs, stream)

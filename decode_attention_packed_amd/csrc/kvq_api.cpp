@@ -204,7 +204,8 @@ namespace {
 int attn_common(const kvq_cache* cache, const float* q, float* out, int n_seq, int n_qtok,
                 int n_q_heads, const int32_t* seg_table, int max_segs, const int32_t* seq_len,
                 int max_seq_len, float sm_scale, int causal, void* workspace, size_t workspace_bytes,
-                const float* k_new, const float* v_new, int n_new, void* stream) {
+                const float* k_new, const float* v_new, int n_new, void* stream,
+                int32_t* dbg_isum = nullptr) {
   int st = check_attn(cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
                       max_seq_len);
   if (st) return st;
@@ -218,7 +219,7 @@ int attn_common(const kvq_cache* cache, const float* q, float* out, int n_seq, i
   if (!aligned16(workspace)) return KVQ_ERR_INVALID;
   const int r = kvq::launch_attn(*cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs,
                                  seq_len, plan, sm_scale, causal ? 1 : 0, workspace, k_new, v_new,
-                                 n_new, static_cast<hipStream_t>(stream));
+                                 n_new, static_cast<hipStream_t>(stream), dbg_isum, max_seq_len);
   return r ? KVQ_ERR_HIP : KVQ_OK;
 }
 
@@ -413,6 +414,16 @@ int kvq_debug_quant_q(const float* q, int n_rows, int head_dim, int8_t* codes, f
                                    static_cast<hipStream_t>(stream))
              ? KVQ_ERR_HIP
              : KVQ_OK;
+}
+
+int kvq_debug_attn_isum(const kvq_cache* cache, const float* q, float* out, int n_seq, int n_qtok,
+                        int n_q_heads, const int32_t* seg_table, int max_segs,
+                        const int32_t* seq_len, int max_seq_len, float sm_scale, int causal,
+                        void* workspace, size_t workspace_bytes, int32_t* isum, void* stream) {
+  if (!isum || !aligned16(isum)) return KVQ_ERR_INVALID;
+  return attn_common(cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
+                     max_seq_len, sm_scale, causal, workspace, workspace_bytes, nullptr, nullptr, 0,
+                     stream, isum);
 }
 
 int kvq_debug_qk_isum(const kvq_cache* cache, const float* q, int n_seq, int n_qtok, int n_q_heads,

@@ -114,7 +114,20 @@ struct AttnParams {
   int xcd_local;          // all splits of a group on one XCD (see block_coords)
   int n_groups_pad;       // groups in the grid: n_seq_groups, rounded up to 8 when xcd_local
   int lpt_seqs;           // > 0: unsplit batch of that many sequences, groups dealt by length
+  // test hook (kvq_debug_attn_isum): the kernels built with DBG store every
+  // per-block int32 Q.K sum of their tiles to
+  // dbg_isum[seq][qtok][q_head][dbg_max_len][D/32]
+  int32_t* dbg_isum;
+  int dbg_max_len;
 };
+
+// Where the debug build stores query row r's block sums (row r of a kv
+// group is query token r / group, head kv_head * group + r % group).
+__device__ __forceinline__ int32_t* dbg_row(const AttnParams& p, int seq, int kvh, int r, int nb) {
+  return p.dbg_isum +
+         (((size_t)seq * p.n_qtok + r / p.group) * p.n_q_heads + kvh * p.group + r % p.group) *
+             (size_t)p.dbg_max_len * nb;
+}
 
 // Chunks from which single calls run the 12-wave build (12 waves x 4 tiles).
 constexpr int kW12MinChunk = 12 * 4 * kTile;
@@ -893,11 +906,11 @@ struct WaveState {
 
 // One 32-token tile from its LDS slot: scores, online softmax update, P.V.
 // P is staged in the slot's K area when it fits, else in `pbuf`.
-template <int D, int VF>
+template <int D, int VF, bool DBG = false>
 __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0, int c1,
                                              const long (&qa)[D / kBlock],
                                              const float (&dqs)[4][D / kBlock], const int (&vis)[4],
-                                             WaveState<D>& st) {
+                                             WaveState<D>& st, int32_t* const (&dbg)[4] = {}) {
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
   constexpr int PSTRIDE = kTile + 4;   // padded row of the P staging tile (floats)
@@ -927,6 +940,13 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const v4i c = qk_block_mfma(qa[b], kb[b]);
+      if constexpr (DBG) {
+        // the test hook: row 4*grp + i, token t0 + r, block b
+        if (t0 + r < c1)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            if (dbg[i]) dbg[i][(size_t)(t0 + r) * NB + b] = c[i];
+      }
       const float dkf = (float)dk[b];
 #pragma unroll
       for (int i = 0; i < 4; ++i) s[h][i] = fmaf((float)c[i], dqs[i][b] * dkf, s[h][i]);
@@ -1028,7 +1048,7 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int D, int VF>
+template <int D, int VF, bool DBG = false>
 __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
@@ -1092,10 +1112,16 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   }
   uint8_t* ring = s_lds + wave * S::NSLOT * S::BYTES;
   float* pbuf = reinterpret_cast<float*>(s_lds + kWaves * S::NSLOT * S::BYTES + wave * S::PBYTES);
+  int32_t* dbg[4] = {};
+  if constexpr (DBG) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * grp + i < R) dbg[i] = dbg_row(p, seq, kvh, 4 * grp + i, NB);
+  }
   auto body = [&](auto slot_c, int t0) {
     constexpr int SL = decltype(slot_c)::value;
     if (t0 + kTile > app.lo && t0 < app.hi) patch_tile<D, VF>(ring + SL * S::BYTES, s_patch, t0, app);
-    process_tile<D, VF>(ring + SL * S::BYTES, pbuf, t0, c1, qa, dqs, vis, st);
+    process_tile<D, VF, DBG>(ring + SL * S::BYTES, pbuf, t0, c1, qa, dqs, vis, st, dbg);
   };
   run_ring<D, VF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
 
@@ -1154,11 +1180,11 @@ __device__ __forceinline__ float sum_blocks(float x) {
 // for fp16 K.
 using QOp = std::conditional_t<kF16K, v8h, long>;
 
-template <int D, int VF>
+template <int D, int VF, bool DBG = false>
 __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, int c1, bool full,
                                                   bool first, int vis, bool valid,
                                                   const QOp (&qb)[D / kBlock], float wq,
-                                                  ColState<D>& st) {
+                                                  ColState<D>& st, int32_t* dbg = nullptr) {
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
   constexpr int NG = D / 16;
@@ -1201,6 +1227,18 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
             slot + S::K_OFF + (tau * S::CPR + (q ^ kswz<S::CPR>(tau))) * 16 + 8 * (grp & 1));
         cq[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ka, qb[bb], cq[h], 0, 0, 0);
       }
+    }
+    if constexpr (DBG) {
+      // the test hook: column (row r, block b) holds that block's sums of
+      // tokens t0 + 8*grp + 4h + i (dbg points at row r's block b)
+      if (valid)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 8 * grp + 4 * h + i;
+            if (t < c1) dbg[(size_t)t * NB] = cq[h][i];
+          }
     }
     const uint4 dkw = *reinterpret_cast<const uint4*>(slot + S::DK_OFF + b * 64 + 16 * grp);
     const uint32_t dkv[4] = {dkw.x, dkw.y, dkw.z, dkw.w};
@@ -1288,7 +1326,7 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
   }
 }
 
-template <int D, int VF>
+template <int D, int VF, bool DBG = false>
 __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
@@ -1359,12 +1397,16 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   st.l = 0.0f;
 
   uint8_t* ring = s_lds + wave * S::NSLOT * S::BYTES;
+  int32_t* dbg = nullptr;
+  if constexpr (DBG) {
+    if (valid) dbg = dbg_row(p, seq, kvh, r, NB) + b;
+  }
   bool first = true;
   auto body = [&](auto slot_c, int t0) {
     constexpr int SL = decltype(slot_c)::value;
     if (t0 + kTile > app.lo && t0 < app.hi) patch_tile<D, VF>(ring + SL * S::BYTES, s_patch, t0, app);
-    process_tile_cols<D, VF>(ring + SL * S::BYTES, t0, c1, t0 + kTile <= vis_min, first, vis, valid,
-                             qb, wq, st);
+    process_tile_cols<D, VF, DBG>(ring + SL * S::BYTES, t0, c1, t0 + kTile <= vis_min, first, vis,
+                                  valid, qb, wq, st, dbg);
     first = false;
   };
   run_ring<D, VF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
@@ -1462,6 +1504,15 @@ template <int D, int VF>
 __global__ __launch_bounds__(kThreads, kOccupancy<D>) void k_attn_cols(AttnParams p) {
   attn_cols_body<D, VF>(p, blockIdx.x);
 }
+// The same kernels with the block-sum store of the test hook.
+template <int D, int VF>
+__global__ __launch_bounds__(kThreads) void k_attn_rows_dbg(AttnParams p) {
+  attn_rows_body<D, VF, true>(p, blockIdx.x);
+}
+template <int D, int VF>
+__global__ __launch_bounds__(kThreads, kOccupancy<D>) void k_attn_cols_dbg(AttnParams p) {
+  attn_cols_body<D, VF, true>(p, blockIdx.x);
+}
 template <int D>
 __global__ __launch_bounds__(64) void k_split_merge(AttnParams p) {
   split_merge_body<D>(p, blockIdx.x);
@@ -1496,10 +1547,16 @@ static void launch_attn_kernel(AttnParams p, dim3 grid, hipStream_t stream) {
     // column layout (the fp16-K build has no other): the split merge runs in
     // the last work-group of each group
     p.merge_launch = 0;
-    hipLaunchKernelGGL((k_attn_cols<D, VF>), grid, dim3(kThreads), 0, stream, p);
+    if (p.dbg_isum)
+      hipLaunchKernelGGL((k_attn_cols_dbg<D, VF>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((k_attn_cols<D, VF>), grid, dim3(kThreads), 0, stream, p);
   } else {
     p.merge_launch = p.n_split > 1;
-    hipLaunchKernelGGL((k_attn_rows<D, VF>), grid, dim3(kThreads), 0, stream, p);
+    if (p.dbg_isum)
+      hipLaunchKernelGGL((k_attn_rows_dbg<D, VF>), grid, dim3(kThreads), 0, stream, p);
+    else
+      hipLaunchKernelGGL((k_attn_rows<D, VF>), grid, dim3(kThreads), 0, stream, p);
   }
   if (p.merge_launch) hipLaunchKernelGGL((k_split_merge<D>), merge_grid, dim3(64), 0, stream, p);
 }
@@ -1542,6 +1599,8 @@ static AttnParams make_params(const kvq_cache& c, const float* q, float* out, in
   p.xcd_local = p.n_seq_groups % kXcds == 0 || (long long)p.n_seq_groups * plan.n_split <= 64;
   p.n_groups_pad = p.xcd_local ? (p.n_seq_groups + kXcds - 1) / kXcds * kXcds : p.n_seq_groups;
   p.merge_launch = 0;
+  p.dbg_isum = nullptr;
+  p.dbg_max_len = 0;
   // unsplit batches of up to 64 sequences (one lane per sequence when the
   // work-groups rank them; see block_coords): ragged batch 85.5 -> 75.7 us
   p.lpt_seqs = (plan.n_split == 1 && n_seq >= 2 && n_seq <= 64 && p.n_groups_pad == p.n_seq_groups) ? n_seq : 0;
@@ -1551,17 +1610,21 @@ static AttnParams make_params(const kvq_cache& c, const float* q, float* out, in
 int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
                 const int32_t* seg_table, int max_segs, const int32_t* seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
-                const float* k_new, const float* v_new, int n_new, hipStream_t stream) {
+                const float* k_new, const float* v_new, int n_new, hipStream_t stream,
+                int32_t* dbg_isum, int dbg_max_len) {
 #if KVQ_KFMT == 0 && !KVQ_COLS_Q4_128
   // the column layout with q4_0 V at head_dim 128 runs the 12-wave build
   // when its chunks give every wave at least 4 tiles
   if (c.head_dim == 128 && c.v_format == 0 && n_qtok * (n_q_heads / c.n_kv_heads) * (128 / kBlock) <= 16 &&
       plan.chunk >= kW12MinChunk)
     return w12::launch_attn(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len, plan,
-                            sm_scale, causal, workspace, k_new, v_new, n_new, stream);
+                            sm_scale, causal, workspace, k_new, v_new, n_new, stream, dbg_isum,
+                            dbg_max_len);
 #endif
-  const AttnParams p = make_params(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
-                                   plan, sm_scale, causal, workspace, k_new, v_new, n_new);
+  AttnParams p = make_params(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len, plan,
+                             sm_scale, causal, workspace, k_new, v_new, n_new);
+  p.dbg_isum = dbg_isum;
+  p.dbg_max_len = dbg_max_len;
   const dim3 grid((unsigned)((long long)p.n_groups_pad * plan.n_split));
   if constexpr (KVQ_COLS_Q4_128) {
     if (c.head_dim != 128 || c.v_format != 0) return -4;   // not reached: only those calls come here

@@ -43,11 +43,14 @@ bool attn_supported(int head_dim, int v_format);
 
 // Split-K attention with the split merge fused into the last work-group;
 // with n_new > 0 it first appends k_new / v_new at tokens seq_len - n_new ..
-// seq_len - 1 of every sequence (in the same launch).
+// seq_len - 1 of every sequence (in the same launch).  With dbg_isum the
+// kernels also store every per-block int32 Q.K sum they form
+// (kvq_debug_attn_isum).
 int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
                 const int32_t* seg_table, int max_segs, const int32_t* seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
-                const float* k_new, const float* v_new, int n_new, hipStream_t stream);
+                const float* k_new, const float* v_new, int n_new, hipStream_t stream,
+                int32_t* dbg_isum = nullptr, int dbg_max_len = 0);
 
 // One call of a batched launch (attn_decode_packed_batch), validated.
 struct AttnCall {
@@ -74,7 +77,8 @@ namespace w12 {
 int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
                 const int32_t* seg_table, int max_segs, const int32_t* seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
-                const float* k_new, const float* v_new, int n_new, hipStream_t stream);
+                const float* k_new, const float* v_new, int n_new, hipStream_t stream,
+                int32_t* dbg_isum = nullptr, int dbg_max_len = 0);
 }  // namespace w12
 
 // The same attention kernels compiled for fp16 K rows (kvq_attn_f16k.hip):
@@ -84,7 +88,8 @@ bool attn_supported(int head_dim, int v_format);
 int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
                 const int32_t* seg_table, int max_segs, const int32_t* seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
-                const float* k_new, const float* v_new, int n_new, hipStream_t stream);
+                const float* k_new, const float* v_new, int n_new, hipStream_t stream,
+                int32_t* dbg_isum = nullptr, int dbg_max_len = 0);
 }  // namespace f16k
 
 int launch_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);

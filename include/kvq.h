@@ -283,6 +283,25 @@ int kvq_debug_qk_isum(const kvq_cache* cache, const float* q, int n_seq, int n_q
                       int n_q_heads, const int32_t* seg_table, int max_segs,
                       const int32_t* seq_len, int max_seq_len, int32_t* isum, void* stream);
 
+/*
+ * kvq_debug_attn_isum: test hook.  Runs attn_decode_packed (same arguments,
+ * workspace, split plan, kernel build and output) with kernels that also
+ * store every per-block int32 sum of Q codes times K codes that their tiles
+ * form, as the matrix cores produce it from the K rows in LDS:
+ *   isum    device int32 [n_seq][n_qtok][n_q_heads][max_seq_len][head_dim/32]
+ *           (16-byte aligned); entry [i][j][h][t][b] is written for every
+ *           token t < seq_len[i], every block b and every query head h, and
+ *           is left untouched otherwise.
+ * Page 1 (summary, body): 8-bit K values go four to a word straight into the
+ * integer dot, so these sums are exact integers that a reference must match
+ * bit for bit.  Errors as attn_decode_packed; KVQ_ERR_INVALID for a NULL or
+ * misaligned isum.
+ */
+int kvq_debug_attn_isum(const kvq_cache* cache, const float* q, float* out, int n_seq, int n_qtok,
+                        int n_q_heads, const int32_t* seg_table, int max_segs,
+                        const int32_t* seq_len, int max_seq_len, float sm_scale, int causal,
+                        void* workspace, size_t workspace_bytes, int32_t* isum, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
