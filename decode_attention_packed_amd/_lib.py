@@ -380,7 +380,7 @@ def attn_decode_packed_batch_workspace_size(calls) -> int:
     arr = _batch_calls(calls)
     out = c_size_t(0)
     _check(lib().attn_decode_packed_batch_workspace_size(arr, len(calls), ctypes.byref(out)),
-           "attn_decode_packed_batch_workspace_size", "kvq_debug_attn_isum")
+           "attn_decode_packed_batch_workspace_size")
     return int(out.value)
 
 
