@@ -26,13 +26,15 @@ KVQ_SEG_ALIGN = 64
 KVQ_MAX_QTOK = 16
 KVQ_MAX_APPEND = 16
 KVQ_MAX_BATCH = 4
+KVQ_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 EXPORTS = ("kvq_abi_version", "kvq_status_string", "kvq_cache_bytes", "kv_append_quant",
            "attn_decode_packed_append",
            "attn_decode_packed_workspace_size", "attn_decode_packed", "kvq_debug_quant_q",
            "kvq_debug_qk_isum", "kvq_debug_stream_read", "kvq_f16k_cache_bytes", "kv_append_f16k",
            "attn_decode_f16k_workspace_size", "attn_decode_f16k", "attn_decode_packed_batch",
-           "attn_decode_packed_batch_workspace_size", "kvq_debug_attn_isum")
+           "attn_decode_packed_batch_workspace_size", "kvq_debug_attn_isum",
+           "attn_decode_packed_noalloc")
 
 
 class KvqCacheStruct(ctypes.Structure):
@@ -107,6 +109,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_debug_qk_isum.restype = c_int
         L.kvq_debug_qk_isum.argtypes = [P, c_void_p, c_int, c_int, c_int, c_void_p, c_int, c_void_p,
                                         c_int, c_void_p, c_void_p]
+        L.attn_decode_packed_noalloc.restype = c_int
+        L.attn_decode_packed_noalloc.argtypes = L.attn_decode_packed.argtypes[:-3] + [c_void_p]
         L.kvq_debug_attn_isum.restype = c_int
         L.kvq_debug_attn_isum.argtypes = L.attn_decode_packed.argtypes[:-1] + [c_void_p, c_void_p]
         if L.kvq_abi_version() != 1:
@@ -443,3 +447,18 @@ def kvq_debug_attn_isum(cache: PackedKVCache, q, out, seq_len, max_seq_len: int,
         return fn(*args[:-1], _ptr(isum), args[-1])
     _attend(call, "kvq_debug_attn_isum", cache, q, out, seq_len, max_seq_len, sm_scale, causal,
             workspace, seg_table, max_segs, stream)
+
+
+def attn_decode_packed_noalloc(cache: PackedKVCache, q, out, seq_len, max_seq_len: int,
+                               sm_scale: float, causal: bool, seg_table=None,
+                               max_segs: int | None = None, stream=None) -> None:
+    """attn_decode_packed without a workspace argument: the library's static
+    device scratch array (KVQ_NOALLOC_SCRATCH_BYTES per GPU) holds the split
+    partials; nothing is allocated."""
+    fn = lib().attn_decode_packed_noalloc
+
+    def call(*args):
+        # drop the workspace pointer and size that _attend passes
+        return fn(*args[:-3], args[-1])
+    _attend(call, "attn_decode_packed_noalloc", cache, q, out, seq_len, max_seq_len, sm_scale,
+            causal, None, seg_table, max_segs, stream)

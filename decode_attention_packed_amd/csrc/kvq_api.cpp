@@ -1,6 +1,8 @@
 // C ABI of libkvq: host-side validation, split planning and launches.
 // Every check runs before the first launch, so an error return leaves device
-// memory untouched.  The library keeps no state and never allocates.
+// memory untouched.  The library never allocates; its only state is the
+// static scratch array of attn_decode_packed_noalloc and, per device, that
+// array's address.
 
 #include <hip/hip_runtime.h>
 
@@ -8,6 +10,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
+#include <mutex>
 
 #include "kvq.h"
 #include "kvq_launch.h"
@@ -311,6 +314,72 @@ int attn_decode_packed_batch(const kvq_attn_call* calls, int n_calls, void* work
   return kvq::launch_attn_batch(c, plans, n_calls, workspace, static_cast<hipStream_t>(stream))
              ? KVQ_ERR_HIP
              : KVQ_OK;
+}
+
+// ---------------------------------------------------------------------------
+// attn_decode_packed_noalloc: the workspace is a static device array
+// ---------------------------------------------------------------------------
+//
+// `scratch` is this library's own device memory, one copy per GPU, held
+// until the process ends.  In host code its name is only a host-side
+// stand-in, so kernels and fills get the address that hipGetSymbolAddress
+// reports for the current device, looked up once per device and kept.
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device, or null when the
+// runtime cannot report it.
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// Zero-fill of the split counters at the front of the scratch array (a
+// kernel rather than hipMemsetAsync, so the call can be captured in a graph).
+__global__ __launch_bounds__(256) void k_zero_words(unsigned* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+}  // namespace
+
+int attn_decode_packed_noalloc(const kvq_cache* cache, const float* q, float* out, int n_seq,
+                               int n_qtok, int n_q_heads, const int32_t* seg_table, int max_segs,
+                               const int32_t* seq_len, int max_seq_len, float sm_scale, int causal,
+                               void* stream) {
+  int st = check_attn(cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
+                      max_seq_len);
+  if (st) return st;
+  if (!std::isfinite(sm_scale)) return KVQ_ERR_INVALID;
+  if (n_qtok * (n_q_heads / cache->n_kv_heads) > KVQ_MAX_QTOK) return KVQ_ERR_UNSUPPORTED;
+  if (!kvq::attn_supported(cache->head_dim, cache->v_format)) return KVQ_ERR_UNSUPPORTED;
+  const kvq::SplitPlan plan = kvq::plan_splits(*cache, n_seq, n_qtok, n_q_heads, max_seq_len);
+  const kvq::WorkspaceLayout ws = kvq::workspace_layout(*cache, n_seq, n_qtok, n_q_heads, plan);
+  if (ws.total > (size_t)KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
+  void* base = scratch_ptr();
+  if (!base) return KVQ_ERR_HIP;
+  // the array keeps the previous call's bytes: its counters must start at zero
+  const int words = (int)(ws.part_o / sizeof(unsigned));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipLaunchKernelGGL(k_zero_words, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, s,
+                     static_cast<unsigned*>(base), words);
+  if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
+  const int r = kvq::launch_attn(*cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs,
+                                 seq_len, plan, sm_scale, causal ? 1 : 0, base, nullptr, nullptr, 0,
+                                 s);
+  return r ? KVQ_ERR_HIP : KVQ_OK;
 }
 
 int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n_seq, int n_qtok,

@@ -16,8 +16,9 @@
  *    the host before anything is launched, so an error return has no side
  *    effects on device memory.
  *  - Pointers named "device" point to GPU memory owned by the caller; the
- *    library never allocates, frees, synchronizes, prints or keeps state.
- *    Device pointers must be 16-byte aligned.
+ *    library never allocates, frees, synchronizes or prints.  Its only state
+ *    is the static scratch array of attn_decode_packed_noalloc and that
+ *    array's address per device.  Device pointers must be 16-byte aligned.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
  *    asynchronously on it; device faults surface at the caller's next sync.
  *  - Contents of device index arrays (segment tables, lengths, positions) are
@@ -163,6 +164,33 @@ int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n
                        int n_qtok, int n_q_heads, const int32_t* seg_table, int max_segs,
                        const int32_t* seq_len, int max_seq_len, float sm_scale, int causal,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * attn_decode_packed_noalloc: attn_decode_packed for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It takes no workspace: the split
+ * partials and counters live in a static device array of this library,
+ * KVQ_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends.  The call
+ * allocates and frees nothing; it enqueues a small fill kernel that zeroes
+ * the counters, then the attention kernels, on `stream`.
+ *   Arguments, layout, output and errors are those of attn_decode_packed,
+ *   except: KVQ_ERR_WORKSPACE when the call's workspace
+ *   (attn_decode_packed_workspace_size) exceeds KVQ_NOALLOC_SCRATCH_BYTES,
+ *   before anything is launched; KVQ_ERR_HIP when the array's device address
+ *   cannot be obtained.  The output equals attn_decode_packed's bit for bit
+ *   (same kernels, same split plan).
+ *   The device current on the calling thread must be the one `stream` and
+ *   the buffers belong to; its copy of the array is looked up on that
+ *   device's first call and kept.
+ *   Every call on one GPU shares that GPU's array: calls that may overlap in
+ *   time on one GPU (different streams, or threads) race and give undefined
+ *   results; calls in order on one stream are safe.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+int attn_decode_packed_noalloc(const kvq_cache* cache, const float* q, float* out, int n_seq,
+                               int n_qtok, int n_q_heads, const int32_t* seg_table, int max_segs,
+                               const int32_t* seq_len, int max_seq_len, float sm_scale, int causal,
+                               void* stream);
 
 /*
  * attn_decode_packed_append: one decode step that first appends new rows and

@@ -241,3 +241,29 @@ def test_batch_args_rejected():
     st, two = size([call(c128), call(c128, hq=16)])
     assert st == K.KVQ_OK and two > one
     assert run([call(c128), call(c128, hq=16)], ws_bytes=two - 16) == K.KVQ_ERR_WORKSPACE
+
+
+def _noalloc(c, q=0x5000, out=0x6000, n_seq=1, n_qtok=1, hq=32, table=None, max_segs=1,
+             seq_len=0x7000, max_len=1024, scale=0.1):
+    return K.lib().attn_decode_packed_noalloc(ctypes.byref(c), q, out, n_seq, n_qtok, hq, table,
+                                              max_segs, seq_len, max_len, scale, 0, None)
+
+
+def test_noalloc_rejects_before_any_launch():
+    """The allocation-free variant checks its arguments as attn_decode_packed
+    does, and refuses a call whose workspace would not fit the static scratch
+    array, all before it asks the runtime for anything."""
+    c = _fake_cache()
+    assert K.KVQ_NOALLOC_SCRATCH_BYTES == 8 << 20
+    assert _noalloc(c, hq=12) == K.KVQ_ERR_INVALID
+    assert _noalloc(c, n_qtok=5) == K.KVQ_ERR_UNSUPPORTED
+    assert _noalloc(c, q=0x5008) == K.KVQ_ERR_INVALID
+    assert _noalloc(c, scale=float("inf")) == K.KVQ_ERR_INVALID
+    assert _noalloc(c, n_seq=0) == K.KVQ_ERR_INVALID
+    # 128 sequences x 8 kv heads x 16 query rows x head_dim 128, unsplit:
+    # 8 MiB of partials alone, over the limit
+    size = ctypes.c_size_t(0)
+    assert K.lib().attn_decode_packed_workspace_size(ctypes.byref(c), 128, 4, 32, 1024,
+                                                     ctypes.byref(size)) == 0
+    assert size.value > K.KVQ_NOALLOC_SCRATCH_BYTES
+    assert _noalloc(c, n_seq=128, n_qtok=4, table=0x9000) == K.KVQ_ERR_WORKSPACE
