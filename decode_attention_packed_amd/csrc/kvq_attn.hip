@@ -715,6 +715,18 @@ __device__ __forceinline__ v8h bytes_to_f16x8(uint32_t w0, uint32_t w1, _Float16
 // overwrites a register the MFMA still reads as its accumulator input only
 // for instructions it emits itself, and it reuses such a dead accumulator
 // register for the next value right after the MFMA issues.
+// The softmax weights enter P.V scaled by 2^kPvShift (p <= 2^kPvShift
+// instead of p <= 1; the running sum l carries the same factor, so o / l and
+// the split merge are unchanged).  It keeps p * d_v out of the fp16
+// subnormal range for small V: with d_v about max|V| / 8 (q4_0) or
+// max|V| / 127 (q8_0), a 1e-2 V scale at 128k tokens put most weights below
+// 6.1e-5 and gave ~7e-3 relative error in the output (q8_0).  The bound it
+// sets: p * d_v <= 2^kPvShift * d_v must stay below the fp16 maximum, i.e.
+// max|V| of a block up to ~32000 for either format (the two shifts differ by
+// the formats' step ratio, 16).
+template <int VF>
+constexpr float kPvShift = VF == 0 ? 4.0f : 8.0f;
+
 __device__ __forceinline__ uint32_t round_f16_pair(float p0, float p1, uint32_t dpair) {
   const v2h d = __builtin_bit_cast(v2h, dpair);
   const v2h r = {(_Float16)__builtin_fmaf(p0, (float)d.x, 0.0f), (_Float16)__builtin_fmaf(p1, (float)d.y, 0.0f)};
@@ -978,11 +990,14 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
   float* sP = S::P_IN_K ? reinterpret_cast<float*>(slot + S::K_OFF) : pbuf;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  float mshift[4];   // the running maxima less the P.V shift
+#pragma unroll
+  for (int i = 0; i < 4; ++i) mshift[i] = mrow[i] - kPvShift<VF>;
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float e = __builtin_amdgcn_exp2f(s[h][i] - mrow[i]);
+      const float e = __builtin_amdgcn_exp2f(s[h][i] - mshift[i]);
       lrow[i] += e;
       sP[(4 * grp + i) * PSTRIDE + 16 * h + col] = e;
     }
@@ -1156,9 +1171,9 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
 
 // Per-lane state: acc[g][i] = sum over tokens of p * V for dim 16g + 4*(l/16)
 // + i of this lane's column; m is the row's running maximum (log2 domain),
-// c0 = -m on the block-0 lane of a live row (so the block sum yields score - m)
-// and -1e30 on the block-0 lane of a padding column; l sums this lane's
-// weights.
+// c0 = kPvShift - m on the block-0 lane of a live row (so the block sum
+// yields score - m + kPvShift) and -1e30 on the block-0 lane of a padding
+// column; l sums this lane's weights (each 2^kPvShift times p).
 template <int D>
 struct ColState {
   v4f acc[D / 16];
@@ -1258,14 +1273,15 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
   }
   float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
   if (!valid) mx = -INFINITY;
-  if (first || __any(mx > 0.0f)) {
+  constexpr float kShift = kPvShift<VF>;
+  if (first || __any(mx > kShift)) {
     // row maximum over the four lane groups (the block lanes agree already)
     const float rm = across32(across16(mx, fmax2), fmax2);
     float delta;
     if (first) {
-      delta = rm == -INFINITY ? 0.0f : rm;   // nothing accumulated yet
+      delta = rm == -INFINITY ? 0.0f : rm - kShift;   // nothing accumulated yet
     } else {
-      delta = fmaxf(rm, 0.0f);
+      delta = fmaxf(rm - kShift, 0.0f);
       const float a = __builtin_amdgcn_exp2f(-delta);
 #pragma unroll
       for (int g = 0; g < NG; ++g) st.acc[g] *= a;
@@ -1393,7 +1409,7 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
 #pragma unroll
   for (int g = 0; g < NG; ++g) st.acc[g] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
   st.m = 0.0f;
-  st.c0 = (b == 0 && !valid) ? -1e30f : 0.0f;
+  st.c0 = b != 0 ? 0.0f : (valid ? kPvShift<VF> : -1e30f);
   st.l = 0.0f;
 
   uint8_t* ring = s_lds + wave * S::NSLOT * S::BYTES;

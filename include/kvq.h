@@ -134,7 +134,12 @@ int attn_decode_packed_workspace_size(const kvq_cache* cache, int n_seq, int n_q
                                       int n_q_heads, int max_seq_len, size_t* bytes);
 
 /*
- * attn_decode_packed: one decode step of attention over the packed cache.
+ * attn_decode_packed: one decode step of attention over the packed cache
+ * (page 1, "Flash Attention for llama.cpp on RDNA3 ... Part 1": summary and
+ * first body paragraph -- the kernel reads the 8-bit K payload, four values
+ * per 32-bit word, with its fp16 scale and feeds it straight into an integer
+ * dot product, with no fp16 K buffer; body and KLD tables -- V as q4_0 or
+ * q8_0; the title's flash attention -- an online softmax over the context).
  *   q        device float [n_seq][n_qtok][n_q_heads][head_dim]
  *   out      device float [n_seq][n_qtok][n_q_heads][head_dim]
  *   seq_len  device int32 [n_seq], each in [max(1, n_qtok), max_seq_len]
@@ -154,7 +159,11 @@ int attn_decode_packed_workspace_size(const kvq_cache* cache, int n_seq, int n_q
  * each (sequence, kv head), or, for more than 4 query rows per kv head at
  * head_dim 128 (8 at 64), by a second launch on the same stream.
  * n_qtok * (n_q_heads / n_kv_heads) must be at most 16 (KVQ_ERR_UNSUPPORTED
- * otherwise).  The split plan depends only on the shape arguments (n_seq,
+ * otherwise).  The weights enter P.V as fp16 values 2^s * p * d_v (s = 4 for
+ * q4_0, 8 for q8_0, cancelled by the normalization), which keeps small V
+ * accurate (relative error at V scaled by 1e-3 as at unit scale) and
+ * requires every cached V block's largest magnitude to be below 32000;
+ * larger values overflow the fp16 operand (undefined output).  The split plan depends only on the shape arguments (n_seq,
  * n_qtok, n_q_heads, max_seq_len and the cache geometry; the environment
  * variable KVQ_CHUNK_TOKENS, a multiple of 256, overrides its split size for
  * tests); for a given plan the output bits are a pure function of the

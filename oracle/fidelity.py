@@ -109,6 +109,28 @@ def workload_report(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float
             "max_dp": dp, "rel_l2": rel}
 
 
+def output_error(q: np.ndarray, k: np.ndarray, v: np.ndarray, sm_scale: float, out: np.ndarray,
+                 kv_heads=None) -> float:
+    """Relative L2 error of a given attention output `out` [Tq][Hq][D] (for
+    example a GPU kernel's) against the exact attention of the unquantized
+    fp32 inputs q [Tq][Hq][D], k and v [L][Hkv][D], over the query heads of
+    the chosen kv heads (all by default), every row seeing all L tokens: the
+    same denominator as workload_report's output columns."""
+    Tq, Hq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    heads = range(Hkv) if kv_heads is None else kv_heads
+    num = den = 0.0
+    for h in heads:
+        qr = q[:, h * G:(h + 1) * G, :].reshape(Tq * G, D).astype(np.float64)
+        w = _softmax_rows((qr @ k[:, h, :].astype(np.float64).T) * float(sm_scale))
+        oe = w @ v[:, h, :].astype(np.float64)
+        o = np.asarray(out[:, h * G:(h + 1) * G, :], dtype=np.float64).reshape(Tq * G, D)
+        num += float(np.sum((o - oe) ** 2))
+        den += float(np.sum(oe * oe))
+    return float(np.sqrt(num / den))
+
+
 def _workloads_module():
     """The seeded input generators, loaded from their file so that the
     library package (and its HIP binding) is not imported."""

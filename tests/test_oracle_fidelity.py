@@ -76,3 +76,20 @@ def test_kl_rows_definition():
     kl = F.kl_rows(p, r)
     assert kl[1] == 0.0
     assert abs(kl[0] - (0.5 * np.log(2.0) + 0.5 * np.log(0.5 / 0.75))) < 1e-15
+
+
+def test_output_error_agrees_with_report_columns():
+    """output_error of the oracle's own method output reproduces the
+    report's int8 column (the same denominator, the same exact reference)."""
+    q, k, v = _inputs(14)
+    sc = D ** -0.5
+    r = F.workload_report(q[None], k[:, None], v[:, None], sc)
+    kw, kd = O.encode_k(k)
+    for fmt, name in ((O.V_Q4_0, "q4_0"), (O.V_Q8_0, "q8_0")):
+        vp, vd = O.encode_v(v, fmt)
+        out = O.decode_attention(q[None, None], kw[None, None], kd[None, None], vp[None, None],
+                                 vd[None, None], fmt, [L], sc, False)[0]
+        e = F.output_error(q[None], k[:, None], v[:, None], sc, out)
+        assert abs(e - r["rel_l2"][("int8", name)]) <= 1e-12 * max(1.0, e)
+    assert F.output_error(q[None], k[:, None], v[:, None], sc,
+                          F.group_report(q, k, v, sc)["outs"][("exact", "exact")][None]) == 0.0
