@@ -181,7 +181,10 @@ def algorithmic_bytes(spec, n_tokens: int, append_rows: int) -> dict:
 
 def _build_cache(K, torch, ci):
     """One packed cache holding every sequence of `ci`, filled by bulk
-    kv_append_quant through each sequence's segment list."""
+    kv_append_quant through each sequence's segment list.  Returns the cache
+    and the segment table the attention calls take: the workload's own for
+    segmented caches, None for contiguous ones (one segment per sequence,
+    the table-free form of the ABI)."""
     spec = ci.spec
     cache = K.PackedKVCache(spec.n_kv_heads, spec.head_dim, ci.seg_tokens, ci.n_segs, spec.v_format)
     if ci.seg_table is not None:
@@ -197,7 +200,7 @@ def _build_cache(K, torch, ci):
         K.kv_append_quant(cache, torch.from_numpy(np.ascontiguousarray(k[None])).cuda(),
                           torch.from_numpy(np.ascontiguousarray(v[None])).cuda(), zero,
                           seg_table=table[i:i + 1])
-    return cache, table
+    return cache, (table if ci.seg_table is not None else None)
 
 
 def other_configs(K, W, torch, stream, steps: int, warmup: int) -> list:

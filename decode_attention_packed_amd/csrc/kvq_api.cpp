@@ -221,8 +221,9 @@ int attn_common(const kvq_cache* cache, const float* q, float* out, int n_seq, i
   if (workspace_bytes < need || !workspace) return KVQ_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KVQ_ERR_INVALID;
   const int r = kvq::launch_attn(*cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs,
-                                 seq_len, plan, sm_scale, causal ? 1 : 0, workspace, k_new, v_new,
-                                 n_new, static_cast<hipStream_t>(stream), dbg_isum, max_seq_len);
+                                 seq_len, max_seq_len, plan, sm_scale, causal ? 1 : 0, workspace,
+                                 k_new, v_new, n_new, static_cast<hipStream_t>(stream), dbg_isum,
+                                 max_seq_len);
   return r ? KVQ_ERR_HIP : KVQ_OK;
 }
 
@@ -377,8 +378,8 @@ int attn_decode_packed_noalloc(const kvq_cache* cache, const float* q, float* ou
                      static_cast<unsigned*>(base), words);
   if (hipGetLastError() != hipSuccess) return KVQ_ERR_HIP;
   const int r = kvq::launch_attn(*cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs,
-                                 seq_len, plan, sm_scale, causal ? 1 : 0, base, nullptr, nullptr, 0,
-                                 s);
+                                 seq_len, max_seq_len, plan, sm_scale, causal ? 1 : 0, base, nullptr,
+                                 nullptr, 0, s);
   return r ? KVQ_ERR_HIP : KVQ_OK;
 }
 
@@ -461,8 +462,9 @@ int attn_decode_f16k(const kvq_cache* cache, const float* q, float* out, int n_s
   if (workspace_bytes < need || !workspace) return KVQ_ERR_WORKSPACE;
   if (!aligned16(workspace)) return KVQ_ERR_INVALID;
   const int r = kvq::f16k::launch_attn(*cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs,
-                                       seq_len, plan, sm_scale, causal ? 1 : 0, workspace, nullptr,
-                                       nullptr, 0, static_cast<hipStream_t>(stream));
+                                       seq_len, max_seq_len, plan, sm_scale, causal ? 1 : 0,
+                                       workspace, nullptr, nullptr, 0,
+                                       static_cast<hipStream_t>(stream));
   return r ? KVQ_ERR_HIP : KVQ_OK;
 }
 

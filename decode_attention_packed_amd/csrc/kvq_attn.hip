@@ -114,6 +114,7 @@ struct AttnParams {
   int xcd_local;          // all splits of a group on one XCD (see block_coords)
   int n_groups_pad;       // groups in the grid: n_seq_groups, rounded up to 8 when xcd_local
   int lpt_seqs;           // > 0: unsplit batch of that many sequences, groups dealt by length
+  int max_len;            // the call's bound on seq_len (host argument)
   // test hook (kvq_debug_attn_isum): the kernels built with DBG store every
   // per-block int32 Q.K sum of their tiles to
   // dbg_isum[seq][qtok][q_head][dbg_max_len][D/32]
@@ -612,21 +613,22 @@ __device__ __forceinline__ void write_appended(const AttnParams& p, int seq, int
   }
 }
 
-// Common prologue: this wave's Q rows (wave, wave + kWaves) go to its last
+// Common prologue, in two parts around the load of the sequence's length.
+//
+// prologue_issue: this wave's Q rows (wave, wave + kWaves) go to its last
 // slot as fp32 ahead of its first tiles, so waiting for them leaves the tiles
-// in flight; then they are quantized (a = max|q|, d = a / 127 in fp32) into
-// codes and scales shared through wave 0's last slot.  Rows past `rows` load
-// row 0 and quantize as zeros.  Issues the wave's static tiles (q.cur, and
-// q.n1 when three slots allow it) and returns after the barrier that
-// publishes the codes.
+// in flight; the appended rows (if any) for the length `Ls`, then the wave's
+// static first tiles (q.cur, and q.n1 when three slots allow it) that start
+// below `cs1`.  Rows past `rows` load row 0.  Returns the tiles issued.
+// Without a segment table these loads need not wait for the length: `Ls`
+// and `cs1` may come from the call's max_seq_len, every token below it lies
+// inside the cache, and tiles past the real end are masked or never used.
 template <int D, int VF>
-__device__ __forceinline__ void prologue(const AttnParams& p, uint8_t* s_lds, int seq, int kvh,
-                                         int wave, int L, int c1, const AppendRange& app,
-                                         uint8_t* s_patch, const TileLane<D, VF>& tl,
-                                         TileCursor& cur, const TileQueue& q, int8_t*& s_qc,
-                                         float*& s_qd) {
+__device__ __forceinline__ int prologue_issue(const AttnParams& p, uint8_t* s_lds, int seq, int kvh,
+                                              int wave, int Ls, int cs1, const AppendRange& app_s,
+                                              const TileLane<D, VF>& tl, TileCursor& cur,
+                                              const TileQueue& q) {
   using S = Slot<D, VF>;
-  constexpr int NB = D / kBlock;
   constexpr int NSLOT = S::NSLOT;
   constexpr int RPW = S::RPW;            // Q rows per wave
   constexpr int PIECES = RPW * D / 4;   // 16-byte pieces of them
@@ -649,11 +651,39 @@ __device__ __forceinline__ void prologue(const AttnParams& p, uint8_t* s_lds, in
   }
   // appended rows, ahead of the tiles so that waiting for them leaves the
   // tiles in flight
-  if (app.hi > app.lo) stage_appended<D, VF>(p, seq, kvh, L, wave, app, ring_lds + (NSLOT - 1) * S::BYTES + S::STAGE);
-  const int n_pro = (q.cur < c1) + (NSLOT == 3 && q.n1 < c1);
-  if (q.cur < c1) issue_tile<D, VF>(p, seq, kvh, q.cur, ring_lds, tl, cur);
-  if (NSLOT == 3 && q.n1 < c1) issue_tile<D, VF>(p, seq, kvh, q.n1, ring_lds + S::BYTES, tl, cur);
-  wait_tiles<S::LPT>(n_pro);
+  if (app_s.hi > app_s.lo)
+    stage_appended<D, VF>(p, seq, kvh, Ls, wave, app_s, ring_lds + (NSLOT - 1) * S::BYTES + S::STAGE);
+  const int n = (q.cur < cs1) + (NSLOT == 3 && q.n1 < cs1);
+  if (q.cur < cs1) issue_tile<D, VF>(p, seq, kvh, q.cur, ring_lds, tl, cur);
+  if (NSLOT == 3 && q.n1 < cs1) issue_tile<D, VF>(p, seq, kvh, q.n1, ring_lds + S::BYTES, tl, cur);
+  return n;
+}
+
+// prologue_finish: with the length L known, stages the appended rows again
+// if the guess `Ls` staged other ones (after the tiles, so it then waits for
+// everything), waits for the Q rows, quantizes them (a = max|q|, d = a / 127
+// in fp32) into codes and scales shared through wave 0's last slot, quantizes
+// the appended rows into the patch buffer, and returns after the barrier that
+// publishes the codes.
+template <int D, int VF>
+__device__ __forceinline__ void prologue_finish(const AttnParams& p, uint8_t* s_lds, int seq, int kvh,
+                                                int wave, int L, int Ls, const AppendRange& app,
+                                                const AppendRange& app_s, int n_issued,
+                                                uint8_t* s_patch, int8_t*& s_qc, float*& s_qd) {
+  using S = Slot<D, VF>;
+  constexpr int NB = D / kBlock;
+  constexpr int NSLOT = S::NSLOT;
+  constexpr int RPW = S::RPW;
+  const int lane = __lane_id();
+  const int R = p.rows;
+  uint8_t* ring = s_lds + wave * NSLOT * S::BYTES;
+  const bool restage = app.hi > app.lo && (L != Ls || app.lo != app_s.lo || app.hi != app_s.hi);
+  if (restage) {
+    stage_appended<D, VF>(p, seq, kvh, L, wave, app, lds_addr(ring) + (NSLOT - 1) * S::BYTES + S::STAGE);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  } else {
+    wait_tiles<S::LPT>(n_issued);
+  }
 
   const float* s_qf = reinterpret_cast<const float*>(ring + (NSLOT - 1) * S::BYTES);
   s_qc = reinterpret_cast<int8_t*>(s_lds + (NSLOT - 1) * S::BYTES + S::QSTAGE);
@@ -682,6 +712,51 @@ __device__ __forceinline__ void prologue(const AttnParams& p, uint8_t* s_lds, in
     quantize_appended<D, VF>(app, wave, reinterpret_cast<const float*>(ring + (NSLOT - 1) * S::BYTES + S::STAGE),
                              s_patch);
   __syncthreads();
+}
+
+// The start of a work-group: coordinates, the first loads and the length.
+// Without a segment table (and without length-ordered dealing, which reads
+// every length first) Q, the first tiles and the appended rows go out
+// before the length is known, taking the call's max_seq_len for it: the
+// length's load is a memory round trip at the head of every work-group's
+// critical path.  A work-group whose split turns out to lie past the end
+// waits for those loads before it leaves (its LDS must not be written after
+// it is freed).  Returns false for such a work-group.
+struct WgStart {
+  int seq, kvh, split, L, n_split_seq, c0, c1;
+  bool off_xcd;
+  AppendRange app;
+};
+template <int D, int VF>
+__device__ __forceinline__ bool wg_start(const AttnParams& p, int blk, uint8_t* s_lds, int wave,
+                                         uint8_t* s_patch, const TileLane<D, VF>& tl,
+                                         TileCursor& cur, TileQueue& tq, int8_t*& s_qc,
+                                         float*& s_qd, WgStart& w) {
+  const BlockCoords bc = block_coords(p, blk);
+  if (bc.pad) return false;
+  w.split = bc.split;
+  w.kvh = bc.kvh;
+  w.seq = bc.seq;
+  w.off_xcd = bc.off_xcd;
+  w.c0 = w.split * p.chunk;
+  const bool guess = bc.len < 0 && p.seg_table == nullptr;
+  const int Ls = bc.len >= 0 ? bc.len : (guess ? p.max_len : load_uniform(p.seq_len + w.seq));
+  if (w.c0 >= Ls) return false;   // no tokens here even at the bound
+  tq = first_tiles(w.c0, wave);
+  const int cs1 = min(w.c0 + p.chunk, Ls);
+  const AppendRange app_s = append_range(p, Ls, w.c0, cs1);
+  const int n_issued = prologue_issue<D, VF>(p, s_lds, w.seq, w.kvh, wave, Ls, cs1, app_s, tl, cur, tq);
+  w.L = guess ? load_uniform(p.seq_len + w.seq) : Ls;
+  w.n_split_seq = min((w.L + p.chunk - 1) / p.chunk, p.n_split);   // clamp: see k_split_merge
+  if (w.split >= w.n_split_seq) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    return false;
+  }
+  w.c1 = min(w.c0 + p.chunk, w.L);
+  w.app = append_range(p, w.L, w.c0, w.c1);
+  prologue_finish<D, VF>(p, s_lds, w.seq, w.kvh, wave, w.L, Ls, w.app, app_s, n_issued, s_patch, s_qc,
+                         s_qd);
+  return true;
 }
 
 // Four bytes -> two fp16 pairs (1024 + byte) placed as [b0, b1] and [b2, b3].
@@ -1080,25 +1155,19 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const BlockCoords bc = block_coords(p, blk);
-  if (bc.pad) return;
-  const int split = bc.split, kvh = bc.kvh, seq = bc.seq;
-  const int L = bc.len >= 0 ? bc.len : load_uniform(p.seq_len + seq);
-  const int n_split_seq = min((L + p.chunk - 1) / p.chunk, p.n_split);   // clamp: see k_split_merge
-  if (split >= n_split_seq) return;
-  const int c0 = split * p.chunk;
-  const int c1 = min(c0 + p.chunk, L);
-  const int R = p.rows, G = p.group;
   const TileLane<D, VF> tl = tile_lane_offsets<D, VF>(lane);
   TileCursor cur = {-1, 0};
-  TileQueue tq = first_tiles(c0, wave);
+  TileQueue tq;
   const uint32_t ring_lds = lds_addr(s_lds + wave * S::NSLOT * S::BYTES);
-
   int8_t* s_qc;
   float* s_qd;
-  const AppendRange app = append_range(p, L, c0, c1);
   uint8_t* s_patch = s_lds + RING;
-  prologue<D, VF>(p, s_lds, seq, kvh, wave, L, c1, app, s_patch, tl, cur, tq, s_qc, s_qd);
+  WgStart ws;
+  if (!wg_start<D, VF>(p, blk, s_lds, wave, s_patch, tl, cur, tq, s_qc, s_qd, ws)) return;
+  const int split = ws.split, kvh = ws.kvh, seq = ws.seq, L = ws.L, n_split_seq = ws.n_split_seq;
+  const int c1 = ws.c1;
+  const AppendRange app = ws.app;
+  const int R = p.rows, G = p.group;
   long qa[NB];
   load_q_operands<D>(s_qc, qa);
   float dqs[4][NB];
@@ -1139,6 +1208,8 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
     process_tile<D, VF, DBG>(ring + SL * S::BYTES, pbuf, t0, c1, qa, dqs, vis, st, dbg);
   };
   run_ring<D, VF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
+  // a tile issued before the length was known and past it may still land
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- this wave's rows to LDS for the merge
   float* s_buf = reinterpret_cast<float*>(s_lds);
@@ -1162,7 +1233,7 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
     }
   }
   __syncthreads();
-  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq, bc.off_xcd);
+  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq, ws.off_xcd);
 }
 
 // ---------------------------------------------------------------------------
@@ -1359,25 +1430,19 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, grp = lane >> 4;
-  const BlockCoords bc = block_coords(p, blk);
-  if (bc.pad) return;
-  const int split = bc.split, kvh = bc.kvh, seq = bc.seq;
-  const int L = bc.len >= 0 ? bc.len : load_uniform(p.seq_len + seq);
-  const int n_split_seq = min((L + p.chunk - 1) / p.chunk, p.n_split);   // clamp: see k_split_merge
-  if (split >= n_split_seq) return;
-  const int c0 = split * p.chunk;
-  const int c1 = min(c0 + p.chunk, L);
-  const int R = p.rows, G = p.group;
   const TileLane<D, VF> tl = tile_lane_offsets<D, VF>(lane);
   TileCursor cur = {-1, 0};
-  TileQueue tq = first_tiles(c0, wave);
+  TileQueue tq;
   const uint32_t ring_lds = lds_addr(s_lds + wave * S::NSLOT * S::BYTES);
-
   int8_t* s_qc;
   float* s_qd;
-  const AppendRange app = append_range(p, L, c0, c1);
   uint8_t* s_patch = s_lds + RING;
-  prologue<D, VF>(p, s_lds, seq, kvh, wave, L, c1, app, s_patch, tl, cur, tq, s_qc, s_qd);
+  WgStart ws;
+  if (!wg_start<D, VF>(p, blk, s_lds, wave, s_patch, tl, cur, tq, s_qc, s_qd, ws)) return;
+  const int split = ws.split, kvh = ws.kvh, seq = ws.seq, L = ws.L, n_split_seq = ws.n_split_seq;
+  const int c1 = ws.c1;
+  const AppendRange app = ws.app;
+  const int R = p.rows, G = p.group;
 
   // column (row r, block b); B operands hold row r's Q codes of block bb in
   // the columns of block bb only
@@ -1426,6 +1491,8 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
     first = false;
   };
   run_ring<D, VF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
+  // a tile issued before the length was known and past it may still land
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
   // ---- this wave's rows to LDS for the merge
   float* s_buf = reinterpret_cast<float*>(s_lds);
@@ -1449,7 +1516,7 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
     }
   }
   __syncthreads();
-  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq, bc.off_xcd);
+  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq, ws.off_xcd);
 }
 
 // ---------------------------------------------------------------------------
@@ -1579,9 +1646,9 @@ static void launch_attn_kernel(AttnParams p, dim3 grid, hipStream_t stream) {
 
 static AttnParams make_params(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok,
                               int n_q_heads, const int32_t* seg_table, int max_segs,
-                              const int32_t* seq_len, const SplitPlan& plan, float sm_scale,
-                              int causal, void* workspace, const float* k_new, const float* v_new,
-                              int n_new) {
+                              const int32_t* seq_len, int max_seq_len, const SplitPlan& plan,
+                              float sm_scale, int causal, void* workspace, const float* k_new,
+                              const float* v_new, int n_new) {
   AttnParams p;
   const WorkspaceLayout ws = workspace_layout(c, n_seq, n_qtok, n_q_heads, plan);
   char* base = static_cast<char*>(workspace);
@@ -1617,6 +1684,7 @@ static AttnParams make_params(const kvq_cache& c, const float* q, float* out, in
   p.merge_launch = 0;
   p.dbg_isum = nullptr;
   p.dbg_max_len = 0;
+  p.max_len = max_seq_len;
   // unsplit batches of up to 64 sequences (one lane per sequence when the
   // work-groups rank them; see block_coords): ragged batch 85.5 -> 75.7 us
   p.lpt_seqs = (plan.n_split == 1 && n_seq >= 2 && n_seq <= 64 && p.n_groups_pad == p.n_seq_groups) ? n_seq : 0;
@@ -1624,7 +1692,7 @@ static AttnParams make_params(const kvq_cache& c, const float* q, float* out, in
 }
 
 int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
-                const int32_t* seg_table, int max_segs, const int32_t* seq_len,
+                const int32_t* seg_table, int max_segs, const int32_t* seq_len, int max_seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
                 const float* k_new, const float* v_new, int n_new, hipStream_t stream,
                 int32_t* dbg_isum, int dbg_max_len) {
@@ -1633,12 +1701,12 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
   // when its chunks give every wave at least 4 tiles
   if (c.head_dim == 128 && c.v_format == 0 && n_qtok * (n_q_heads / c.n_kv_heads) * (128 / kBlock) <= 16 &&
       plan.chunk >= kW12MinChunk)
-    return w12::launch_attn(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len, plan,
-                            sm_scale, causal, workspace, k_new, v_new, n_new, stream, dbg_isum,
-                            dbg_max_len);
+    return w12::launch_attn(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
+                            max_seq_len, plan, sm_scale, causal, workspace, k_new, v_new, n_new,
+                            stream, dbg_isum, dbg_max_len);
 #endif
-  AttnParams p = make_params(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len, plan,
-                             sm_scale, causal, workspace, k_new, v_new, n_new);
+  AttnParams p = make_params(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
+                             max_seq_len, plan, sm_scale, causal, workspace, k_new, v_new, n_new);
   p.dbg_isum = dbg_isum;
   p.dbg_max_len = dbg_max_len;
   const dim3 grid((unsigned)((long long)p.n_groups_pad * plan.n_split));
@@ -1689,7 +1757,8 @@ int launch_attn_batch(const AttnCall* calls, const SplitPlan* plans, int n_calls
   for (int i = 0; i < n_calls; ++i) {
     const AttnCall& a = calls[i];
     b.p[i] = make_params(*a.cache, a.q, a.out, a.n_seq, a.n_qtok, a.n_q_heads, a.seg_table, a.max_segs,
-                         a.seq_len, plans[i], a.sm_scale, a.causal, base, nullptr, nullptr, 0);
+                         a.seq_len, a.max_seq_len, plans[i], a.sm_scale, a.causal, base, nullptr,
+                         nullptr, 0);
     base += workspace_layout(*a.cache, a.n_seq, a.n_qtok, a.n_q_heads, plans[i]).total;
     b.count[i] = b.p[i].n_groups_pad * plans[i].n_split;
     b.start[i + 1] = b.start[i] + (b.count[i] + kXcds - 1) / kXcds * kXcds;

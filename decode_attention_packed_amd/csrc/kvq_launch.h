@@ -47,7 +47,7 @@ bool attn_supported(int head_dim, int v_format);
 // kernels also store every per-block int32 Q.K sum they form
 // (kvq_debug_attn_isum).
 int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
-                const int32_t* seg_table, int max_segs, const int32_t* seq_len,
+                const int32_t* seg_table, int max_segs, const int32_t* seq_len, int max_seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
                 const float* k_new, const float* v_new, int n_new, hipStream_t stream,
                 int32_t* dbg_isum = nullptr, int dbg_max_len = 0);
@@ -75,7 +75,7 @@ int launch_attn_batch(const AttnCall* calls, const SplitPlan* plans, int n_calls
 // work-group (kvq_attn_w12.hip); launch_attn above hands those calls to it.
 namespace w12 {
 int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
-                const int32_t* seg_table, int max_segs, const int32_t* seq_len,
+                const int32_t* seg_table, int max_segs, const int32_t* seq_len, int max_seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
                 const float* k_new, const float* v_new, int n_new, hipStream_t stream,
                 int32_t* dbg_isum = nullptr, int dbg_max_len = 0);
@@ -86,7 +86,7 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
 namespace f16k {
 bool attn_supported(int head_dim, int v_format);
 int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
-                const int32_t* seg_table, int max_segs, const int32_t* seq_len,
+                const int32_t* seg_table, int max_segs, const int32_t* seq_len, int max_seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
                 const float* k_new, const float* v_new, int n_new, hipStream_t stream,
                 int32_t* dbg_isum = nullptr, int dbg_max_len = 0);
