@@ -32,7 +32,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "decode_attention_packed_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_traffic_long128k.txt")
+PROFILES = os.path.join(ROOT, "profiles")
+TRAFFIC_FILE = os.path.join(PROFILES, "attn_traffic_long128k.txt")
 CALIB_BYTES = 256 << 20   # known sizes read / written by the calibration kernels
 ATTN_KERNEL = "kvq::w12::k_attn_cols<128, 0>"   # the 12-wave build that runs the step
 
@@ -47,20 +48,28 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def read_traffic() -> int | None:
-    """Calibrated HBM bytes per attention launch from the committed counter
-    summary, or None when it is missing or stale."""
+def _read_summary(path: str) -> dict | None:
+    """key = value lines of a committed counter summary, or None when it is
+    missing or was measured on other kernel sources."""
     try:
         kv = {}
-        with open(TRAFFIC_FILE) as fh:
+        with open(path) as fh:
             for line in fh:
                 if "=" in line and not line.startswith("#"):
                     k, v = line.split("=", 1)
-                    kv[k.strip()] = v.strip()
-        if kv.get("kernel_source_sha256") != kernel_source_hash():
-            return None
-        return int(float(kv["attn_traffic_bytes"]))
-    except (OSError, KeyError, ValueError):
+                    kv[k.strip()] = v.split("#", 1)[0].strip()
+        return kv if kv.get("kernel_source_sha256") == kernel_source_hash() else None
+    except OSError:
+        return None
+
+
+def read_traffic(workload: str = "long128k") -> int | None:
+    """Calibrated HBM bytes per launch of the workload's step from the
+    committed counter summary, or None when it is missing or stale."""
+    kv = _read_summary(os.path.join(PROFILES, f"attn_traffic_{workload}.txt"))
+    try:
+        return int(float(kv["attn_traffic_bytes"])) if kv else None
+    except (KeyError, ValueError):
         return None
 
 
@@ -76,9 +85,11 @@ def _counter_rows(d: str, counter: str) -> dict:
     return out
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str, fetch_cmd: str, write_cmd: str) -> str:
-    """Turn the FETCH_SIZE and WRITE_SIZE runs (of `bench.py --calibrate`)
-    into the traffic summary: each counter is scaled by what it reads for a
+def summarize_pmc(fetch_dir: str, write_dir: str, fetch_cmd: str, write_cmd: str,
+                  workload: str = "long128k") -> str:
+    """Turn the FETCH_SIZE and WRITE_SIZE runs (of `bench.py --calibrate`, or
+    `bench.py --profile WORKLOAD --calibrate`) into the traffic summary of the
+    workload's step kernels: each counter is scaled by what it reads for a
     kernel of known size (the library's stream-read kernel over CALIB_BYTES
     for fetches, a device copy of CALIB_BYTES for writes)."""
     fetch = _counter_rows(fetch_dir, "FETCH_SIZE")
@@ -102,17 +113,11 @@ def summarize_pmc(fetch_dir: str, write_dir: str, fetch_cmd: str, write_cmd: str
     cp = pick(write, "copyBuffer")
     cp = [v for v in cp if v >= 0.5 * max(cp)] if cp else cp
     cp_kib, n_cp = med(cp, "the calibration copy")
-    at_f, n_af = med(pick(fetch, ATTN_KERNEL), ATTN_KERNEL)
-    at_w, n_aw = med(pick(write, ATTN_KERNEL), ATTN_KERNEL)
     ffac = CALIB_BYTES / (rd_kib * 1024)
     wfac = CALIB_BYTES / (cp_kib * 1024)
-    fb = at_f * 1024 * ffac
-    wb = at_w * 1024 * wfac
-    from decode_attention_packed_amd import workloads as W
-    alg = algorithmic_bytes(W.WORKLOADS["long128k"].caches[0], 131072, 1)["step"]
+    info = PROFILE_INFO[workload]
     lines = [
-        "# HBM traffic of one launch of the step kernel (append one token + attention) on the",
-        "# long128k workload, from rocprofv3",
+        f"# HBM traffic of one {info['what']}, from rocprofv3",
         "# counters (KiB per dispatch, medians), each scaled by the same counter read",
         f"# for a kernel of known size ({CALIB_BYTES} bytes read / written).",
         f"# fetch run: {fetch_cmd}",
@@ -122,32 +127,71 @@ def summarize_pmc(fetch_dir: str, write_dir: str, fetch_cmd: str, write_cmd: str
         f"calib_copy_write_kib = {cp_kib:.1f}   # device copy, {n_cp} dispatches",
         f"fetch_factor = {ffac:.4f}",
         f"write_factor = {wfac:.4f}",
-        f"attn_fetch_kib = {at_f:.1f}   # {ATTN_KERNEL}, {n_af} dispatches",
-        f"attn_write_kib = {at_w:.1f}   # {n_aw} dispatches",
-        f"attn_fetch_bytes = {fb:.0f}",
-        f"attn_write_bytes = {wb:.0f}",
-        f"attn_traffic_bytes = {fb + wb:.0f}",
-        f"algorithmic_bytes = {alg}",
-        f"traffic_over_algorithmic = {(fb + wb) / alg:.4f}",
     ]
+    fb = wb = 0.0
+    for kern in info["kernels"]:
+        kf, n_f = med(pick(fetch, kern), kern)
+        kw, n_w = med(pick(write, kern), kern)
+        lines += [f"fetch_kib = {kf:.1f}   # {kern}, {n_f} dispatches",
+                  f"write_kib = {kw:.1f}   # {kern}, {n_w} dispatches"]
+        fb += kf * 1024 * ffac
+        wb += kw * 1024 * wfac
+    alg = info["bytes"]
+    lines += [f"attn_fetch_bytes = {fb:.0f}", f"attn_write_bytes = {wb:.0f}",
+              f"attn_traffic_bytes = {fb + wb:.0f}", f"algorithmic_bytes = {alg}",
+              f"traffic_over_algorithmic = {(fb + wb) / alg:.4f}"]
     return "\n".join(lines) + "\n"
 
 
-def summarize_trace(trace_dir: str, cmd: str, steps: int, warmup: int) -> str:
+# SQ counters collected in one pass (at most 8 SQ and 2 GRBM counters).
+SQ_COUNTERS = ("SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+               "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+               "GRBM_GUI_ACTIVE")
+
+
+def summarize_sq(workload: str, sq_dir: str, cmd: str) -> str:
+    """Per-dispatch medians of the SQ counters of the workload's main kernel,
+    per 32-token tile and wave (each tile is processed by exactly one wave)."""
+    info = PROFILE_INFO[workload]
+    kern = info["kernels"][0]
+    lines = [f"# SQ counters of {kern} ({info['what']}), rocprofv3, medians per dispatch;",
+             f"# per tile = divided by the {info['tiles']} 32-token tiles (x query-row groups) a launch processes.",
+             f"# command: {cmd}",
+             f"kernel_source_sha256 = {kernel_source_hash()}"]
+    vals = {}
+    for c in SQ_COUNTERS:
+        v = [x for k, xs in _counter_rows(sq_dir, c).items() if kern in k for x in xs]
+        if v:
+            vals[c] = float(np.median(v))
+            lines.append(f"{c.lower()} = {vals[c]:.0f}   # {len(v)} dispatches")
+    for c in ("SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_MFMA", "SQ_INSTS_LDS"):
+        if c in vals:
+            lines.append(f"{c.lower()}_per_tile = {vals[c] / info['tiles']:.1f}")
+    if "SQ_LDS_BANK_CONFLICT" in vals and vals.get("SQ_LDS_IDX_ACTIVE"):
+        lines.append(f"lds_bank_conflict_over_active = "
+                     f"{vals['SQ_LDS_BANK_CONFLICT'] / vals['SQ_LDS_IDX_ACTIVE']:.4f}")
+    return "\n".join(lines) + "\n"
+
+
+def summarize_trace(trace_dir: str, cmd: str, steps: int, warmup: int,
+                    workload: str = "long128k") -> str:
     """Per-kernel statistics of a `rocprofv3 --kernel-trace --stats` run of
-    this benchmark, with the attention kernel's durations split by bench
-    phase (cold rotating replicas, per-step events, warm single replica)."""
+    this benchmark (the full run: the attention kernel's durations are also
+    split by bench phase) or of `bench.py --profile WORKLOAD`."""
     stats = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
     trace = glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True)
     if not stats or not trace:
         raise SystemExit(f"no kernel trace under {trace_dir}")
-    lines = ["# Kernel durations of the long128k decode step (bench.py) from rocprofv3.",
+    what = PROFILE_INFO[workload]["what"] if "--profile" in cmd else "long128k decode step (bench.py)"
+    lines = [f"# Kernel durations of the {what} from rocprofv3.",
              f"# command: {cmd}",
              "# kernel | calls | average us | min us | max us"]
     with open(stats[0]) as fh:
         for row in csv.DictReader(fh):
             lines.append(f"{row['Name'][:90]} | {row['Calls']} | {float(row['AverageNs']) / 1e3:.2f} | "
                          f"{float(row['MinNs']) / 1e3:.2f} | {float(row['MaxNs']) / 1e3:.2f}")
+    if "--profile" in cmd:
+        return "\n".join(lines) + "\n"
     with open(trace[0]) as fh:
         rows = sorted(csv.DictReader(fh), key=lambda r: int(r["Start_Timestamp"]))
     att = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
@@ -177,6 +221,58 @@ def algorithmic_bytes(spec, n_tokens: int, append_rows: int) -> dict:
     attn = n_tokens * spec.n_kv_heads * (kb + vb)
     app = append_rows * spec.n_kv_heads * (kb + vb)
     return {"attn": attn, "append": app, "step": attn + app, "per_token_head": kb + vb}
+
+
+def _ragged_lengths() -> np.ndarray:
+    """The ragged workload's sequence lengths, drawn from its seed as
+    workloads.make_inputs draws them (without drawing Q, K and V)."""
+    from decode_attention_packed_amd import workloads as W
+    wl = W.WORKLOADS["ragged"]
+    ra = np.random.Generator(np.random.PCG64(np.random.SeedSequence(wl.seed).spawn(4)[3]))
+    return W.ragged_lengths(ra, wl.caches[0].n_seq, hi=wl.caches[0].ctx)
+
+
+def _profile_info() -> dict:
+    """Per workload: what one step is, the kernels that run it (the first is
+    the main one), algorithmic KV bytes per step and the 32-token tiles (per
+    kv head and query-row group) one step processes."""
+    from decode_attention_packed_amd import workloads as W
+    wl = W.WORKLOADS
+    lens = _ragged_lengths()
+    rg = wl["ragged"].caches[0]
+    per = lambda spec: algorithmic_bytes(spec, 1, 0)["per_token_head"]   # noqa: E731
+    return {
+        "long128k": dict(what="long128k step (append one token + attention over 131072 tokens, one launch)",
+                         kernels=(ATTN_KERNEL,),
+                         bytes=algorithmic_bytes(wl["long128k"].caches[0], 131072, 1)["step"], tiles=4096 * 8),
+        "tiny": dict(what="tiny decode call (512 tokens, 1 kv head)", kernels=("kvq::k_attn_cols<128, 0>",),
+                     bytes=512 * per(wl["tiny"].caches[0]), tiles=16),
+        "gqa8k_q4_0": dict(what="gqa8k call with q4_0 V (8192 tokens, 8 kv heads)",
+                           kernels=("kvq::k_attn_cols<128, 0>",),
+                           bytes=8192 * 8 * per(wl["gqa8k"].caches[0]), tiles=256 * 8),
+        "gqa8k_q8_0": dict(what="gqa8k call with q8_0 V (8192 tokens, 8 kv heads)",
+                           kernels=("kvq::k_attn_cols<128, 1>",),
+                           bytes=8192 * 8 * per(wl["gqa8k"].caches[1]), tiles=256 * 8),
+        "verify128k": dict(what="verify step (main and draft caches at 131072 tokens, one batched launch "
+                                "and its split-merge launch)",
+                           kernels=("kvq::k_attn_rows_batch<128, 0>", "kvq::k_split_merge_batch<128>"),
+                           bytes=131072 * (8 + 4) * per(wl["verify128k"].caches[0]), tiles=4096 * 12),
+        "ragged": dict(what="ragged batch call (16 sequences, 32 kv heads, head_dim 64, q8_0 V)",
+                       kernels=("kvq::k_attn_cols<64, 1>",),
+                       bytes=int(lens.sum()) * 32 * per(rg), tiles=int(((lens + 31) // 32).sum()) * 32),
+    }
+
+
+class _LazyInfo(dict):
+    def __missing__(self, key):
+        self.update(_profile_info())
+        return dict.__getitem__(self, key)
+
+
+PROFILE_INFO = _LazyInfo()
+# other_configs rows whose traffic summaries exist per workload (the verify
+# step's summary covers its batched launch)
+PROFILE_INFO_KEYS = ("tiny", "gqa8k_q4_0", "gqa8k_q8_0", "ragged")
 
 
 def _build_cache(K, torch, ci):
@@ -254,6 +350,9 @@ def other_configs(K, W, torch, stream, steps: int, warmup: int) -> list:
         rows.append({"workload": label, "us_per_step": round(ms * 1e3, 2), "kv_bytes_per_step": nbytes,
                      "gbs": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1),
                      "launches_per_step": len(names), "replicas": reps})
+        if label in PROFILE_INFO_KEYS:
+            tb = read_traffic(label)
+            rows[-1]["traffic_over_algorithmic"] = None if tb is None else round(tb / nbytes, 4)
         print(f"[bench] {label}: {ms * 1e3:.2f} us/step, {gbs:.0f} GB/s", file=sys.stderr, flush=True)
         if len(calls) > 1:
             # the same calls as one attn_decode_packed_batch launch
@@ -273,10 +372,12 @@ def other_configs(K, W, torch, stream, steps: int, warmup: int) -> list:
             torch.cuda.synchronize()
             ms = e0.elapsed_time(e1) / steps
             gbs = nbytes / (ms * 1e-3) / 1e9
+            tb = read_traffic(label)
             rows.append({"workload": label + " (one batched launch)", "us_per_step": round(ms * 1e3, 2),
                          "kv_bytes_per_step": nbytes, "gbs": round(gbs, 1),
                          "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "launches_per_step": 1,
-                         "replicas": reps})
+                         "replicas": reps,
+                         "traffic_over_algorithmic": None if tb is None else round(tb / nbytes, 4)})
             print(f"[bench] {label} batched: {ms * 1e3:.2f} us/step, {gbs:.0f} GB/s", file=sys.stderr,
                   flush=True)
         del calls
@@ -410,6 +511,125 @@ def cpu_baseline(ci, target_s: float = 12.0) -> dict:
                                    f"limited to 1 thread"}}
 
 
+def profile_steps(K, W, torch, stream, workload: str):
+    """The step of one workload as other_configs (or the long128k step) times
+    it, with the same rotating replicas: returns fn(i) that enqueues step i,
+    and the single-call arguments the timeline hook takes (cache, table, q,
+    seq_len, max_seq_len, spec) for its main cache."""
+    reps = {"long128k": 3, "tiny": 1, "gqa8k_q4_0": 24, "gqa8k_q8_0": 18, "verify128k": 2, "ragged": 2}[workload]
+    name = "gqa8k" if workload.startswith("gqa8k") else workload
+    cis = W.make_inputs(name)
+    if workload == "gqa8k_q8_0":
+        cis = cis[1:]
+    elif workload.startswith("gqa8k"):
+        cis = cis[:1]
+    calls = []
+    for ci in cis:
+        built = [_build_cache(K, torch, ci) for _ in range(reps)]
+        q = torch.from_numpy(ci.q).cuda()
+        sl = torch.from_numpy(ci.seq_len).cuda()
+        calls.append((ci, built, q, torch.empty_like(q), sl, int(ci.seq_len.max())))
+    ci0, built0, q0, out0, sl0, mx0 = calls[0]
+    single = (built0[0][0], built0[0][1], q0, sl0, mx0, ci0.spec)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    if workload == "long128k":
+        ak = torch.from_numpy(ci0.extra["append_k"]).cuda()
+        av = torch.from_numpy(ci0.extra["append_v"]).cuda()
+
+        def fn(i):
+            K.attn_decode_packed_append(built0[i % reps][0], q0, ak, av, out0, sl0, mx0,
+                                        ci0.spec.sm_scale, False, ws, stream=stream)
+    elif workload == "verify128k":
+        args = [[dict(cache=b[r][0], q=q, out=o, seq_len=sl, max_seq_len=mx, sm_scale=ci.spec.sm_scale,
+                      causal=ci.spec.causal, seg_table=b[r][1]) for ci, b, q, o, sl, mx in calls]
+                for r in range(reps)]
+
+        def fn(i):
+            K.attn_decode_packed_batch(args[i % reps], ws, stream=stream)
+    else:
+        def fn(i):
+            c, t = built0[i % reps]
+            K.attn_decode_packed(c, q0, out0, sl0, mx0, ci0.spec.sm_scale, ci0.spec.causal, ws,
+                                 seg_table=t, stream=stream)
+    torch.cuda.synchronize()
+    return fn, single
+
+
+def timeline(K, W, torch, stream, workload: str, launches: int, cmd: str) -> str:
+    """Per-phase timeline of the workload's main attention call from the
+    kernels' own timestamps (kvq_debug_attn_timeline; the constant 100 MHz
+    clock, 10 ns), medians over `launches` launches, each preceded by six
+    plain launches so that it starts on a busy device.  The long128k step
+    is timed as its attention call (the hook takes no appended rows), the
+    verify step as its main cache's call."""
+    fn, (cache, table, q, sl, mx, spec) = profile_steps(K, W, torch, stream, workload)
+    if workload == "verify128k":
+        ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+
+        def fn(i):   # noqa: F811  the main cache alone, as single calls
+            K.attn_decode_packed(cache, q, out, sl, mx, spec.sm_scale, spec.causal, ws, seg_table=table,
+                                 stream=stream)
+    out = torch.empty_like(q)
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    hkv = spec.n_kv_heads
+    st = torch.zeros((spec.n_seq, hkv, 64, 8), dtype=torch.int64, device="cuda")
+    for i in range(200):
+        fn(i)
+    rows = []
+    for it in range(launches):
+        st.zero_()
+        for i in range(6):
+            fn(i)
+        K.kvq_debug_attn_timeline(cache, q, out, sl, mx, spec.sm_scale, spec.causal, ws, st,
+                                  seg_table=table, stream=stream)
+        torch.cuda.synchronize()
+        T = st.cpu().numpy().view(np.uint64).astype(np.int64)          # [S][H][split][8]
+        live = T[..., 0] > 0
+        t0 = T[..., 0][live].min()
+        us = lambda x: (x - t0) * 0.01                                   # noqa: E731
+        ent, qr, tile, r0, r1 = (us(T[..., k][live]) for k in range(5))
+        flags = T[..., 7]
+        # per (sequence, kv head) group: the last ring end, and when its output was written
+        g_end, g_done, g_pub = [], [], []
+        for si in range(spec.n_seq):
+            for h in range(hkv):
+                lv = live[si, h]
+                if not lv.any():
+                    continue
+                g_end.append(us(T[si, h, lv, 4].max()))
+                m = lv & ((flags[si, h] & 3) != 0)
+                if m.any():
+                    g_done.append(us(T[si, h, m, 6].max()))
+                    if (flags[si, h][m] & 1).any():
+                        g_pub.append(us(T[si, h, m & ((flags[si, h] & 1) != 0), 5].max()) - g_end[-1])
+        g_end, g_done = np.array(g_end), np.array(g_done)
+        rows.append(dict(last_entry=ent.max(), q_ready=np.median(qr), first_tile=np.median(tile[tile > 0]),
+                         ring_end_wg=np.median(r1), wave_spread=np.median(r1 - r0),
+                         group_end_min=g_end.min(), group_end_max=g_end.max(),
+                         merge_pub=np.median(g_pub) if g_pub else float("nan"),
+                         end=g_done.max() if g_done.size else float("nan"),
+                         tail=(g_done.max() - g_end[np.argmax(g_done)]) if g_done.size else float("nan")))
+    keys = list(rows[0])
+    med = {k: float(np.median([r[k] for r in rows])) for k in keys}
+    info = PROFILE_INFO[workload]
+    lines = [f"# Per-phase timeline of the {info['what']}: attention call only, one launch on a busy device,",
+             "# microseconds after the first work-group's entry (the kernels' own s_memrealtime stamps, 10 ns),",
+             f"# medians over {launches} launches.",
+             f"# command: {cmd}",
+             f"kernel_source_sha256 = {kernel_source_hash()}",
+             f"last_workgroup_entry = {med['last_entry']:.2f}   # every work-group resident",
+             f"q_codes_ready = {med['q_ready']:.2f}   # median work-group: Q loaded, quantized, shared",
+             f"first_tile_ready = {med['first_tile']:.2f}   # median work-group, wave 0",
+             f"workgroup_ring_end = {med['ring_end_wg']:.2f}   # median work-group, its last wave",
+             f"wave_spread_in_workgroup = {med['wave_spread']:.2f}   # first to last wave's ring end",
+             f"group_ring_end_first = {med['group_end_min']:.2f}   # (sequence, kv head) groups: earliest",
+             f"group_ring_end_last = {med['group_end_max']:.2f}   # and latest last ring end",
+             f"merge_counter_back_after_group_end = {med['merge_pub']:.2f}   # merging work-group, median group",
+             f"output_written = {med['end']:.2f}   # the last group's rows written",
+             f"tail_after_last_group_ring_end = {med['tail']:.2f}   # wave merge, publish, split merge"]
+    return "\n".join(lines) + "\n"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -426,19 +646,30 @@ def main() -> int:
                     help="write the kernel-trace summary of a rocprofv3 run of this benchmark and exit")
     ap.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "FETCH_CMD", "WRITE_CMD"),
                     help="write the traffic summary from two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-sq", nargs=2, metavar=("SQ_DIR", "CMD"),
+                    help="write the SQ counter summary of --workload from a rocprofv3 --pmc run and exit")
+    ap.add_argument("--workload", default="long128k",
+                    choices=["long128k", "tiny", "gqa8k_q4_0", "gqa8k_q8_0", "verify128k", "ragged"],
+                    help="the workload --profile, --timeline and the summaries cover")
+    ap.add_argument("--profile", action="store_true",
+                    help="run only --workload's step (W + K launches) for counter or trace runs")
+    ap.add_argument("--timeline", type=int, default=0, metavar="LAUNCHES",
+                    help="write the per-phase timeline of --workload from the kernels' stamps and exit")
     args = ap.parse_args()
+    wl = args.workload
+    summary = None
     if args.summarize_trace:
-        text = summarize_trace(*args.summarize_trace, args.steps, args.warmup)
-        with open(os.path.join(ROOT, "profiles", "attn_kernel_trace_long128k.txt"), "w") as fh:
-            fh.write(text)
-        print(text, end="")
-        return 0
-    if args.summarize_pmc:
-        text = summarize_pmc(*args.summarize_pmc)
-        os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
-        with open(TRAFFIC_FILE, "w") as fh:
-            fh.write(text)
-        print(text, end="")
+        summary = (f"attn_kernel_trace_{wl}.txt",
+                   summarize_trace(*args.summarize_trace, args.steps, args.warmup, wl))
+    elif args.summarize_pmc:
+        summary = (f"attn_traffic_{wl}.txt", summarize_pmc(*args.summarize_pmc, workload=wl))
+    elif args.summarize_sq:
+        summary = (f"attn_sq_{wl}.txt", summarize_sq(wl, *args.summarize_sq))
+    if summary:
+        os.makedirs(PROFILES, exist_ok=True)
+        with open(os.path.join(PROFILES, summary[0]), "w") as fh:
+            fh.write(summary[1])
+        print(summary[1], end="")
         return 0
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only; the path is not "
@@ -451,6 +682,32 @@ def main() -> int:
     from decode_attention_packed_amd import workloads as W
 
     torch.cuda.set_device(0)
+    if args.profile or args.timeline:
+        stream = torch.cuda.current_stream()
+        if args.timeline:
+            cmd = "python3 " + " ".join(sys.argv)
+            text = timeline(K, W, torch, stream, wl, args.timeline, cmd)
+            with open(os.path.join(PROFILES, f"attn_timeline_{wl}.txt"), "w") as fh:
+                fh.write(text)
+            print(text, end="")
+            return 0
+        fn, _ = profile_steps(K, W, torch, stream, wl)
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        for i in range(args.steps):
+            fn(i)
+        torch.cuda.synchronize()
+        if args.calibrate:
+            sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+            a = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+            b = torch.empty_like(a)
+            for _ in range(5):
+                K.kvq_debug_stream_read(a, sink, stream=stream)
+                b.copy_(a)
+            torch.cuda.synchronize()
+        print(f"[bench] profiled {wl}: {args.warmup} + {args.steps} steps", file=sys.stderr, flush=True)
+        return 0
     ci = W.make_inputs("long128k")[0]
     spec = ci.spec
     L = spec.ctx

@@ -12,7 +12,7 @@ from ._lib import (EXPORTS, KVQ_NOALLOC_SCRATCH_BYTES, attn_decode_packed_noallo
                    attn_decode_f16k_workspace_size, kv_append_f16k, kvq_f16k_cache_bytes,
                    attn_decode_packed_batch, attn_decode_packed_batch_workspace_size, KVQ_MAX_BATCH,
                    attn_decode_packed_workspace_size, kv_append_quant, kvq_abi_version,
-                   kvq_cache_bytes, kvq_debug_attn_isum, kvq_debug_qk_isum, kvq_debug_quant_q, kvq_debug_stream_read, lib,
+                   kvq_cache_bytes, kvq_debug_attn_isum, kvq_debug_attn_timeline, kvq_debug_qk_isum, kvq_debug_quant_q, kvq_debug_stream_read, lib,
                    status_string)
 
 __all__ = ["EXPORTS", "KVQ_NOALLOC_SCRATCH_BYTES", "attn_decode_packed_noalloc", "KVQ_BLOCK", "KVQ_ERR_HIP", "KVQ_ERR_INVALID", "KVQ_ERR_UNSUPPORTED",
@@ -22,5 +22,5 @@ __all__ = ["EXPORTS", "KVQ_NOALLOC_SCRATCH_BYTES", "attn_decode_packed_noalloc",
            "attn_decode_f16k_workspace_size", "kv_append_f16k", "kvq_f16k_cache_bytes",
            "attn_decode_packed_batch", "attn_decode_packed_batch_workspace_size", "KVQ_MAX_BATCH",
            "attn_decode_packed_workspace_size", "kv_append_quant", "kvq_abi_version",
-           "kvq_cache_bytes", "kvq_debug_attn_isum", "kvq_debug_qk_isum", "kvq_debug_quant_q", "kvq_debug_stream_read", "lib",
+           "kvq_cache_bytes", "kvq_debug_attn_isum", "kvq_debug_attn_timeline", "kvq_debug_qk_isum", "kvq_debug_quant_q", "kvq_debug_stream_read", "lib",
            "status_string"]

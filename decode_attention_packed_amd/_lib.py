@@ -34,7 +34,7 @@ EXPORTS = ("kvq_abi_version", "kvq_status_string", "kvq_cache_bytes", "kv_append
            "kvq_debug_qk_isum", "kvq_debug_stream_read", "kvq_f16k_cache_bytes", "kv_append_f16k",
            "attn_decode_f16k_workspace_size", "attn_decode_f16k", "attn_decode_packed_batch",
            "attn_decode_packed_batch_workspace_size", "kvq_debug_attn_isum",
-           "attn_decode_packed_noalloc")
+           "attn_decode_packed_noalloc", "kvq_debug_attn_timeline")
 
 
 class KvqCacheStruct(ctypes.Structure):
@@ -111,6 +111,8 @@ def lib() -> ctypes.CDLL:
                                         c_int, c_void_p, c_void_p]
         L.attn_decode_packed_noalloc.restype = c_int
         L.attn_decode_packed_noalloc.argtypes = L.attn_decode_packed.argtypes[:-3] + [c_void_p]
+        L.kvq_debug_attn_timeline.restype = c_int
+        L.kvq_debug_attn_timeline.argtypes = L.attn_decode_packed.argtypes[:-1] + [c_void_p, c_void_p]
         L.kvq_debug_attn_isum.restype = c_int
         L.kvq_debug_attn_isum.argtypes = L.attn_decode_packed.argtypes[:-1] + [c_void_p, c_void_p]
         if L.kvq_abi_version() != 1:
@@ -462,3 +464,18 @@ def attn_decode_packed_noalloc(cache: PackedKVCache, q, out, seq_len, max_seq_le
         return fn(*args[:-3], args[-1])
     _attend(call, "attn_decode_packed_noalloc", cache, q, out, seq_len, max_seq_len, sm_scale,
             causal, None, seg_table, max_segs, stream)
+
+
+def kvq_debug_attn_timeline(cache: PackedKVCache, q, out, seq_len, max_seq_len: int,
+                            sm_scale: float, causal: bool, workspace, stamps, seg_table=None,
+                            max_segs: int | None = None, stream=None) -> None:
+    """attn_decode_packed that also stores per-work-group timestamps: stamps
+    int64 (read as uint64) [n_seq][n_kv_heads][n_split][8], contiguous."""
+    import torch
+    _need(stamps, torch.int64, "stamps")
+    fn = lib().kvq_debug_attn_timeline
+
+    def call(*args):
+        return fn(*args[:-1], _ptr(stamps), args[-1])
+    _attend(call, "kvq_debug_attn_timeline", cache, q, out, seq_len, max_seq_len, sm_scale, causal,
+            workspace, seg_table, max_segs, stream)

@@ -208,7 +208,7 @@ int attn_common(const kvq_cache* cache, const float* q, float* out, int n_seq, i
                 int n_q_heads, const int32_t* seg_table, int max_segs, const int32_t* seq_len,
                 int max_seq_len, float sm_scale, int causal, void* workspace, size_t workspace_bytes,
                 const float* k_new, const float* v_new, int n_new, void* stream,
-                int32_t* dbg_isum = nullptr) {
+                int32_t* dbg_isum = nullptr, unsigned long long* dbg_stamps = nullptr) {
   int st = check_attn(cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
                       max_seq_len);
   if (st) return st;
@@ -223,7 +223,7 @@ int attn_common(const kvq_cache* cache, const float* q, float* out, int n_seq, i
   const int r = kvq::launch_attn(*cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs,
                                  seq_len, max_seq_len, plan, sm_scale, causal ? 1 : 0, workspace,
                                  k_new, v_new, n_new, static_cast<hipStream_t>(stream), dbg_isum,
-                                 max_seq_len);
+                                 max_seq_len, dbg_stamps);
   return r ? KVQ_ERR_HIP : KVQ_OK;
 }
 
@@ -495,6 +495,17 @@ int kvq_debug_attn_isum(const kvq_cache* cache, const float* q, float* out, int 
   return attn_common(cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
                      max_seq_len, sm_scale, causal, workspace, workspace_bytes, nullptr, nullptr, 0,
                      stream, isum);
+}
+
+int kvq_debug_attn_timeline(const kvq_cache* cache, const float* q, float* out, int n_seq,
+                            int n_qtok, int n_q_heads, const int32_t* seg_table, int max_segs,
+                            const int32_t* seq_len, int max_seq_len, float sm_scale, int causal,
+                            void* workspace, size_t workspace_bytes, uint64_t* stamps,
+                            void* stream) {
+  if (!stamps || !aligned16(stamps)) return KVQ_ERR_INVALID;
+  return attn_common(cache, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
+                     max_seq_len, sm_scale, causal, workspace, workspace_bytes, nullptr, nullptr, 0,
+                     stream, nullptr, reinterpret_cast<unsigned long long*>(stamps));
 }
 
 int kvq_debug_qk_isum(const kvq_cache* cache, const float* q, int n_seq, int n_qtok, int n_q_heads,

@@ -120,7 +120,23 @@ struct AttnParams {
   // dbg_isum[seq][qtok][q_head][dbg_max_len][D/32]
   int32_t* dbg_isum;
   int dbg_max_len;
+  // measurement hook (kvq_debug_attn_timeline): the kernels built with the
+  // timeline mode store stamps per work-group (stamp_row)
+  unsigned long long* dbg_stamps;
 };
+
+// The timeline mode's stamps, per work-group, in the device's constant
+// 100 MHz clock (s_memrealtime): entry, Q codes ready (after the prologue's
+// barrier), wave 0's first tile ready, the first and the last wave's ring
+// done, partial published (split counter returned; stores issued for the
+// row layout, whose merge is a second launch), merge or direct output done,
+// and flags (bit 0: this work-group merged the splits, bit 1: a single split
+// wrote its rows directly).
+enum { kStStart, kStQ, kStTile, kStRing0, kStRing1, kStPub, kStDone, kStFlags, kStamps };
+__device__ __forceinline__ unsigned long long* stamp_row(const AttnParams& p, int seq, int kvh, int split) {
+  return p.dbg_stamps + (((size_t)seq * p.n_kv_heads + kvh) * p.n_split + split) * kStamps;
+}
+__device__ __forceinline__ unsigned long long now_stamp() { return __builtin_amdgcn_s_memrealtime(); }
 
 // Where the debug build stores query row r's block sums (row r of a kv
 // group is query token r / group, head kv_head * group + r % group).
@@ -815,7 +831,8 @@ __device__ __forceinline__ uint32_t round_f16_pair(float p0, float p1, uint32_t 
 // sequence with a single split writes its rows directly.
 template <int D, int LDS_BYTES>
 __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, int* s_last, int seq,
-                                             int kvh, int split, int n_split_seq, bool off_xcd) {
+                                             int kvh, int split, int n_split_seq, bool off_xcd,
+                                             unsigned long long* ts = nullptr) {
   constexpr int kBatch = 16;                              // partial loads in flight per thread
   static_assert(kMaxSplits * kRows * 4 + 16 * kThreads <= LDS_BYTES,
                 "split merge does not fit the LDS buffer");
@@ -861,7 +878,13 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, 
     }
   }
   // with the merge as its own launch, the kernel boundary publishes the partials
-  if (single || p.merge_launch) return;
+  if (single || p.merge_launch) {
+    if (ts && tid == 0) {
+      ts[single ? kStDone : kStPub] = now_stamp();
+      ts[kStFlags] = single ? 2u : 0u;
+    }
+    return;
+  }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // The counter's low 16 bits count finished splits; each work-group that is
@@ -872,6 +895,10 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, 
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = (done & 0xFFFFu) == (unsigned)(n_split_seq - 1);
     *s_last = last ? (((done + inc) >> 16) == 0 ? 2 : 1) : 0;
+    if (ts) {
+      ts[kStPub] = now_stamp();
+      ts[kStFlags] = last ? 1u : 0u;
+    }
   }
   __syncthreads();
   if (!*s_last) return;
@@ -965,9 +992,11 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, 
     const int rr = (4 * cc) / D;
     *reinterpret_cast<float4*>(out_row(rr) + (4 * cc - rr * D)) = o;
   }
-  if (tid == 0)
+  if (tid == 0) {
+    if (ts) ts[kStDone] = now_stamp();
     __hip_atomic_store(&p.counters[(size_t)seq * p.n_kv_heads + kvh], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -993,7 +1022,7 @@ struct WaveState {
 
 // One 32-token tile from its LDS slot: scores, online softmax update, P.V.
 // P is staged in the slot's K area when it fits, else in `pbuf`.
-template <int D, int VF, bool DBG = false>
+template <int D, int VF, int DBG = 0>
 __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0, int c1,
                                              const long (&qa)[D / kBlock],
                                              const float (&dqs)[4][D / kBlock], const int (&vis)[4],
@@ -1027,7 +1056,7 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       const v4i c = qk_block_mfma(qa[b], kb[b]);
-      if constexpr (DBG) {
+      if constexpr (DBG == 1) {
         // the test hook: row 4*grp + i, token t0 + r, block b
         if (t0 + r < c1)
 #pragma unroll
@@ -1138,7 +1167,21 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
   __builtin_amdgcn_wave_barrier();
 }
 
-template <int D, int VF, bool DBG = false>
+// The first and the last wave's ring end, from the per-wave stamps (after a
+// barrier; thread 0 writes them).
+__device__ __forceinline__ void ring_end_stamps(const unsigned long long* s_ring_end,
+                                                unsigned long long* ts) {
+  if (threadIdx.x != 0) return;
+  unsigned long long lo = s_ring_end[0], hi = s_ring_end[0];
+  for (int w = 1; w < kWaves; ++w) {
+    lo = s_ring_end[w] < lo ? s_ring_end[w] : lo;
+    hi = s_ring_end[w] > hi ? s_ring_end[w] : hi;
+  }
+  ts[kStRing0] = lo;
+  ts[kStRing1] = hi;
+}
+
+template <int D, int VF, int DBG = 0>
 __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
@@ -1150,7 +1193,9 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
 
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   __shared__ int s_last;
+  __shared__ unsigned long long s_ring_end[DBG == 2 ? kWaves : 1];
 
+  const unsigned long long t_entry = DBG == 2 ? now_stamp() : 0ull;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1168,6 +1213,15 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   const int c1 = ws.c1;
   const AppendRange app = ws.app;
   const int R = p.rows, G = p.group;
+  unsigned long long* ts = nullptr;
+  if constexpr (DBG == 2) {
+    ts = stamp_row(p, seq, kvh, split);
+    if (tid == 0) {
+      ts[kStStart] = t_entry;
+      ts[kStQ] = now_stamp();
+    }
+  }
+  bool first_tile = true;
   long qa[NB];
   load_q_operands<D>(s_qc, qa);
   float dqs[4][NB];
@@ -1197,19 +1251,26 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   uint8_t* ring = s_lds + wave * S::NSLOT * S::BYTES;
   float* pbuf = reinterpret_cast<float*>(s_lds + kWaves * S::NSLOT * S::BYTES + wave * S::PBYTES);
   int32_t* dbg[4] = {};
-  if constexpr (DBG) {
+  if constexpr (DBG == 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (4 * grp + i < R) dbg[i] = dbg_row(p, seq, kvh, 4 * grp + i, NB);
   }
   auto body = [&](auto slot_c, int t0) {
     constexpr int SL = decltype(slot_c)::value;
+    if constexpr (DBG == 2) {
+      if (first_tile && wave == 0 && lane == 0) ts[kStTile] = now_stamp();
+      first_tile = false;
+    }
     if (t0 + kTile > app.lo && t0 < app.hi) patch_tile<D, VF>(ring + SL * S::BYTES, s_patch, t0, app);
     process_tile<D, VF, DBG>(ring + SL * S::BYTES, pbuf, t0, c1, qa, dqs, vis, st, dbg);
   };
   run_ring<D, VF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
   // a tile issued before the length was known and past it may still land
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (DBG == 2) {
+    if (lane == 0) s_ring_end[wave] = now_stamp();
+  }
 
   // ---- this wave's rows to LDS for the merge
   float* s_buf = reinterpret_cast<float*>(s_lds);
@@ -1233,7 +1294,8 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
     }
   }
   __syncthreads();
-  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq, ws.off_xcd);
+  if constexpr (DBG == 2) ring_end_stamps(s_ring_end, ts);
+  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq, ws.off_xcd, ts);
 }
 
 // ---------------------------------------------------------------------------
@@ -1266,7 +1328,7 @@ __device__ __forceinline__ float sum_blocks(float x) {
 // for fp16 K.
 using QOp = std::conditional_t<kF16K, v8h, long>;
 
-template <int D, int VF, bool DBG = false>
+template <int D, int VF, int DBG = 0>
 __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, int c1, bool full,
                                                   bool first, int vis, bool valid,
                                                   const QOp (&qb)[D / kBlock], float wq,
@@ -1314,7 +1376,7 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
         cq[h] = __builtin_amdgcn_mfma_i32_16x16x32_i8(ka, qb[bb], cq[h], 0, 0, 0);
       }
     }
-    if constexpr (DBG) {
+    if constexpr (DBG == 1) {
       // the test hook: column (row r, block b) holds that block's sums of
       // tokens t0 + 8*grp + 4h + i (dbg points at row r's block b)
       if (valid)
@@ -1413,7 +1475,7 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
   }
 }
 
-template <int D, int VF, bool DBG = false>
+template <int D, int VF, int DBG = 0>
 __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
@@ -1425,7 +1487,9 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
 
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   __shared__ int s_last;
+  __shared__ unsigned long long s_ring_end[DBG == 2 ? kWaves : 1];
 
+  const unsigned long long t_entry = DBG == 2 ? now_stamp() : 0ull;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1443,6 +1507,14 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   const int c1 = ws.c1;
   const AppendRange app = ws.app;
   const int R = p.rows, G = p.group;
+  unsigned long long* ts = nullptr;
+  if constexpr (DBG == 2) {
+    ts = stamp_row(p, seq, kvh, split);
+    if (tid == 0) {
+      ts[kStStart] = t_entry;
+      ts[kStQ] = now_stamp();
+    }
+  }
 
   // column (row r, block b); B operands hold row r's Q codes of block bb in
   // the columns of block bb only
@@ -1479,12 +1551,15 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
 
   uint8_t* ring = s_lds + wave * S::NSLOT * S::BYTES;
   int32_t* dbg = nullptr;
-  if constexpr (DBG) {
+  if constexpr (DBG == 1) {
     if (valid) dbg = dbg_row(p, seq, kvh, r, NB) + b;
   }
   bool first = true;
   auto body = [&](auto slot_c, int t0) {
     constexpr int SL = decltype(slot_c)::value;
+    if constexpr (DBG == 2) {
+      if (first && wave == 0 && lane == 0) ts[kStTile] = now_stamp();
+    }
     if (t0 + kTile > app.lo && t0 < app.hi) patch_tile<D, VF>(ring + SL * S::BYTES, s_patch, t0, app);
     process_tile_cols<D, VF, DBG>(ring + SL * S::BYTES, t0, c1, t0 + kTile <= vis_min, first, vis,
                                   valid, qb, wq, st, dbg);
@@ -1493,6 +1568,9 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   run_ring<D, VF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
   // a tile issued before the length was known and past it may still land
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (DBG == 2) {
+    if (lane == 0) s_ring_end[wave] = now_stamp();
+  }
 
   // ---- this wave's rows to LDS for the merge
   float* s_buf = reinterpret_cast<float*>(s_lds);
@@ -1516,7 +1594,8 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
     }
   }
   __syncthreads();
-  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq, ws.off_xcd);
+  if constexpr (DBG == 2) ring_end_stamps(s_ring_end, ts);
+  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq, ws.off_xcd, ts);
 }
 
 // ---------------------------------------------------------------------------
@@ -1587,14 +1666,23 @@ template <int D, int VF>
 __global__ __launch_bounds__(kThreads, kOccupancy<D>) void k_attn_cols(AttnParams p) {
   attn_cols_body<D, VF>(p, blockIdx.x);
 }
-// The same kernels with the block-sum store of the test hook.
+// The same kernels with the block-sum store of the test hook, and with the
+// timeline stamps of the measurement hook.
 template <int D, int VF>
 __global__ __launch_bounds__(kThreads) void k_attn_rows_dbg(AttnParams p) {
-  attn_rows_body<D, VF, true>(p, blockIdx.x);
+  attn_rows_body<D, VF, 1>(p, blockIdx.x);
 }
 template <int D, int VF>
 __global__ __launch_bounds__(kThreads, kOccupancy<D>) void k_attn_cols_dbg(AttnParams p) {
-  attn_cols_body<D, VF, true>(p, blockIdx.x);
+  attn_cols_body<D, VF, 1>(p, blockIdx.x);
+}
+template <int D, int VF>
+__global__ __launch_bounds__(kThreads) void k_attn_rows_tl(AttnParams p) {
+  attn_rows_body<D, VF, 2>(p, blockIdx.x);
+}
+template <int D, int VF>
+__global__ __launch_bounds__(kThreads, kOccupancy<D>) void k_attn_cols_tl(AttnParams p) {
+  attn_cols_body<D, VF, 2>(p, blockIdx.x);
 }
 template <int D>
 __global__ __launch_bounds__(64) void k_split_merge(AttnParams p) {
@@ -1632,12 +1720,16 @@ static void launch_attn_kernel(AttnParams p, dim3 grid, hipStream_t stream) {
     p.merge_launch = 0;
     if (p.dbg_isum)
       hipLaunchKernelGGL((k_attn_cols_dbg<D, VF>), grid, dim3(kThreads), 0, stream, p);
+    else if (p.dbg_stamps)
+      hipLaunchKernelGGL((k_attn_cols_tl<D, VF>), grid, dim3(kThreads), 0, stream, p);
     else
       hipLaunchKernelGGL((k_attn_cols<D, VF>), grid, dim3(kThreads), 0, stream, p);
   } else {
     p.merge_launch = p.n_split > 1;
     if (p.dbg_isum)
       hipLaunchKernelGGL((k_attn_rows_dbg<D, VF>), grid, dim3(kThreads), 0, stream, p);
+    else if (p.dbg_stamps)
+      hipLaunchKernelGGL((k_attn_rows_tl<D, VF>), grid, dim3(kThreads), 0, stream, p);
     else
       hipLaunchKernelGGL((k_attn_rows<D, VF>), grid, dim3(kThreads), 0, stream, p);
   }
@@ -1684,6 +1776,7 @@ static AttnParams make_params(const kvq_cache& c, const float* q, float* out, in
   p.merge_launch = 0;
   p.dbg_isum = nullptr;
   p.dbg_max_len = 0;
+  p.dbg_stamps = nullptr;
   p.max_len = max_seq_len;
   // unsplit batches of up to 64 sequences (one lane per sequence when the
   // work-groups rank them; see block_coords): ragged batch 85.5 -> 75.7 us
@@ -1695,7 +1788,7 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
                 const int32_t* seg_table, int max_segs, const int32_t* seq_len, int max_seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
                 const float* k_new, const float* v_new, int n_new, hipStream_t stream,
-                int32_t* dbg_isum, int dbg_max_len) {
+                int32_t* dbg_isum, int dbg_max_len, unsigned long long* dbg_stamps) {
 #if KVQ_KFMT == 0 && !KVQ_COLS_Q4_128
   // the column layout with q4_0 V at head_dim 128 runs the 12-wave build
   // when its chunks give every wave at least 4 tiles
@@ -1703,12 +1796,13 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
       plan.chunk >= kW12MinChunk)
     return w12::launch_attn(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
                             max_seq_len, plan, sm_scale, causal, workspace, k_new, v_new, n_new,
-                            stream, dbg_isum, dbg_max_len);
+                            stream, dbg_isum, dbg_max_len, dbg_stamps);
 #endif
   AttnParams p = make_params(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
                              max_seq_len, plan, sm_scale, causal, workspace, k_new, v_new, n_new);
   p.dbg_isum = dbg_isum;
   p.dbg_max_len = dbg_max_len;
+  p.dbg_stamps = dbg_stamps;
   const dim3 grid((unsigned)((long long)p.n_groups_pad * plan.n_split));
   if constexpr (KVQ_COLS_Q4_128) {
     if (c.head_dim != 128 || c.v_format != 0) return -4;   // not reached: only those calls come here

@@ -45,12 +45,14 @@ bool attn_supported(int head_dim, int v_format);
 // with n_new > 0 it first appends k_new / v_new at tokens seq_len - n_new ..
 // seq_len - 1 of every sequence (in the same launch).  With dbg_isum the
 // kernels also store every per-block int32 Q.K sum they form
-// (kvq_debug_attn_isum).
+// (kvq_debug_attn_isum); with dbg_stamps, per-work-group timestamps
+// (kvq_debug_attn_timeline).
 int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
                 const int32_t* seg_table, int max_segs, const int32_t* seq_len, int max_seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
                 const float* k_new, const float* v_new, int n_new, hipStream_t stream,
-                int32_t* dbg_isum = nullptr, int dbg_max_len = 0);
+                int32_t* dbg_isum = nullptr, int dbg_max_len = 0,
+                unsigned long long* dbg_stamps = nullptr);
 
 // One call of a batched launch (attn_decode_packed_batch), validated.
 struct AttnCall {
@@ -78,7 +80,8 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
                 const int32_t* seg_table, int max_segs, const int32_t* seq_len, int max_seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
                 const float* k_new, const float* v_new, int n_new, hipStream_t stream,
-                int32_t* dbg_isum = nullptr, int dbg_max_len = 0);
+                int32_t* dbg_isum = nullptr, int dbg_max_len = 0,
+                unsigned long long* dbg_stamps = nullptr);
 }  // namespace w12
 
 // The same attention kernels compiled for fp16 K rows (kvq_attn_f16k.hip):
@@ -89,7 +92,8 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
                 const int32_t* seg_table, int max_segs, const int32_t* seq_len, int max_seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
                 const float* k_new, const float* v_new, int n_new, hipStream_t stream,
-                int32_t* dbg_isum = nullptr, int dbg_max_len = 0);
+                int32_t* dbg_isum = nullptr, int dbg_max_len = 0,
+                unsigned long long* dbg_stamps = nullptr);
 }  // namespace f16k
 
 int launch_debug_stream_read(const void* buf, size_t bytes, uint32_t* sink, hipStream_t stream);

@@ -339,6 +339,30 @@ int kvq_debug_attn_isum(const kvq_cache* cache, const float* q, float* out, int 
                         const int32_t* seq_len, int max_seq_len, float sm_scale, int causal,
                         void* workspace, size_t workspace_bytes, int32_t* isum, void* stream);
 
+/*
+ * kvq_debug_attn_timeline: measurement hook, not part of the method.  Runs
+ * attn_decode_packed (same arguments, split plan, kernel build and output)
+ * with kernels that also store timestamps of the device's constant 100 MHz
+ * clock per work-group:
+ *   stamps  device uint64 [n_seq][n_kv_heads][n_split][8], 16-byte aligned;
+ *           n_split is the call's split count (at most 64, so
+ *           n_seq * n_kv_heads * 512 entries always suffice).  Entries of
+ *           work-group (i, h, s): 0 entry, 1 Q codes ready, 2 wave 0's first
+ *           tile ready, 3 the first and 4 the last wave's ring done, 5 partial
+ *           published (split counter returned; stores issued when the merge
+ *           is a second launch), 6 merge or direct output done, 7 flags
+ *           (bit 0: this work-group merged the splits, bit 1: a single split
+ *           wrote its rows directly).  Work-groups past a sequence's end
+ *           write nothing.
+ * Errors as attn_decode_packed; KVQ_ERR_INVALID for a NULL or misaligned
+ * stamps buffer.
+ */
+int kvq_debug_attn_timeline(const kvq_cache* cache, const float* q, float* out, int n_seq,
+                            int n_qtok, int n_q_heads, const int32_t* seg_table, int max_segs,
+                            const int32_t* seq_len, int max_seq_len, float sm_scale, int causal,
+                            void* workspace, size_t workspace_bytes, uint64_t* stamps,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -153,3 +153,34 @@ def test_w12_131073_tokens_all_heads():
     got, cache = run_fused(ci, 1)
     check_appended_rows(cache, ci, 1)
     _all_heads(ci, got, "w12 131073 fused all heads")
+
+
+@pytest.mark.parametrize("name,ctx", [("tiny", None), ("gqa8k", 4096), ("verify128k", 3000)])
+def test_timeline_hook(name, ctx):
+    """kvq_debug_attn_timeline runs the same kernels as attn_decode_packed
+    (bit-identical output) and stores, for every work-group that has tokens,
+    stamps in phase order: entry <= Q ready <= ring ends, and a merge or
+    direct-output stamp for exactly one work-group per (sequence, kv head)."""
+    ci = W.make_inputs(name, ctx=ctx)[0]
+    spec = ci.spec
+    cache, table, max_segs = H.build_cache(ci)
+    table = _table(ci, max_segs)
+    q, sl, mx = H.dev(ci.q), H.dev(ci.seq_len), int(ci.seq_len.max())
+    ws = torch.zeros(max(16, K.attn_decode_packed_workspace_size(cache, spec.n_seq, spec.n_qtok,
+                                                                 spec.n_q_heads, mx)),
+                     dtype=torch.uint8, device="cuda")
+    st = torch.zeros((spec.n_seq, spec.n_kv_heads, 64, 8), dtype=torch.int64, device="cuda")
+    out, ref = torch.empty_like(q), torch.empty_like(q)
+    K.kvq_debug_attn_timeline(cache, q, out, sl, mx, spec.sm_scale, spec.causal, ws, st, seg_table=table)
+    K.attn_decode_packed(cache, q, ref, sl, mx, spec.sm_scale, spec.causal, ws, seg_table=table)
+    torch.cuda.synchronize()
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), ref.cpu().numpy().view(np.uint32))
+    T = st.cpu().numpy().view(np.uint64).astype(np.int64)
+    live = T[..., 0] > 0
+    assert live.any()
+    for k in (1, 3, 4):
+        assert np.all(T[..., k][live] >= T[..., 0][live])
+    assert np.all(T[..., 4][live] >= T[..., 3][live]) and np.all(T[..., 3][live] >= T[..., 1][live])
+    merged = live & ((T[..., 7] & 3) != 0)
+    assert np.array_equal(merged.sum(axis=2), np.ones(merged.shape[:2], int)) or spec.n_qtok * (
+        spec.n_q_heads // spec.n_kv_heads) * (spec.head_dim // 32) > 16   # row layout: merge launch
