@@ -470,7 +470,7 @@ def kvq_debug_attn_timeline(cache: PackedKVCache, q, out, seq_len, max_seq_len: 
                             sm_scale: float, causal: bool, workspace, stamps, seg_table=None,
                             max_segs: int | None = None, stream=None) -> None:
     """attn_decode_packed that also stores per-work-group timestamps: stamps
-    int64 (read as uint64) [n_seq][n_kv_heads][n_split][8], contiguous."""
+    int64 (read as uint64) [n_seq][n_kv_heads][64][8], contiguous."""
     import torch
     _need(stamps, torch.int64, "stamps")
     fn = lib().kvq_debug_attn_timeline

@@ -125,7 +125,8 @@ struct AttnParams {
   unsigned long long* dbg_stamps;
 };
 
-// The timeline mode's stamps, per work-group, in the device's constant
+// The timeline mode's stamps, per work-group ([sequence][kv head][split, up
+// to kMaxSplits][kStamps]), in the device's constant
 // 100 MHz clock (s_memrealtime): entry, Q codes ready (after the prologue's
 // barrier), wave 0's first tile ready, the first and the last wave's ring
 // done, partial published (split counter returned; stores issued for the
@@ -134,7 +135,7 @@ struct AttnParams {
 // wrote its rows directly).
 enum { kStStart, kStQ, kStTile, kStRing0, kStRing1, kStPub, kStDone, kStFlags, kStamps };
 __device__ __forceinline__ unsigned long long* stamp_row(const AttnParams& p, int seq, int kvh, int split) {
-  return p.dbg_stamps + (((size_t)seq * p.n_kv_heads + kvh) * p.n_split + split) * kStamps;
+  return p.dbg_stamps + (((size_t)seq * p.n_kv_heads + kvh) * kMaxSplits + split) * kStamps;
 }
 __device__ __forceinline__ unsigned long long now_stamp() { return __builtin_amdgcn_s_memrealtime(); }
 

@@ -344,9 +344,8 @@ int kvq_debug_attn_isum(const kvq_cache* cache, const float* q, float* out, int 
  * attn_decode_packed (same arguments, split plan, kernel build and output)
  * with kernels that also store timestamps of the device's constant 100 MHz
  * clock per work-group:
- *   stamps  device uint64 [n_seq][n_kv_heads][n_split][8], 16-byte aligned;
- *           n_split is the call's split count (at most 64, so
- *           n_seq * n_kv_heads * 512 entries always suffice).  Entries of
+ *   stamps  device uint64 [n_seq][n_kv_heads][64][8], 16-byte aligned
+ *           (64: the most splits a call makes).  Entries of
  *           work-group (i, h, s): 0 entry, 1 Q codes ready, 2 wave 0's first
  *           tile ready, 3 the first and 4 the last wave's ring done, 5 partial
  *           published (split counter returned; stores issued when the merge
