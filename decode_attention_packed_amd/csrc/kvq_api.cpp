@@ -135,7 +135,7 @@ WorkspaceLayout workspace_layout(const kvq_cache& c, int n_seq, int n_qtok, int 
   const size_t groups = (size_t)n_seq * c.n_kv_heads;
   WorkspaceLayout w;
   w.counters = 0;
-  w.part_o = round256(groups * sizeof(unsigned));
+  w.part_o = round256(groups * kCounterStride * sizeof(unsigned));
   w.part_ml = w.part_o + round256(groups * plan.n_split * rows * c.head_dim * sizeof(float));
   w.total = w.part_ml + round256(groups * plan.n_split * rows * 2 * sizeof(float));
   return w;

@@ -892,7 +892,7 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, 
   // not on its group's XCD also adds 1 << 16.
   if (tid == 0) {
     const unsigned inc = 1u + (off_xcd ? (1u << 16) : 0u);
-    const unsigned done = __hip_atomic_fetch_add(&p.counters[(size_t)seq * p.n_kv_heads + kvh], inc,
+    const unsigned done = __hip_atomic_fetch_add(&p.counters[((size_t)seq * p.n_kv_heads + kvh) * kCounterStride], inc,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = (done & 0xFFFFu) == (unsigned)(n_split_seq - 1);
     *s_last = last ? (((done + inc) >> 16) == 0 ? 2 : 1) : 0;
@@ -995,7 +995,7 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, 
   }
   if (tid == 0) {
     if (ts) ts[kStDone] = now_stamp();
-    __hip_atomic_store(&p.counters[(size_t)seq * p.n_kv_heads + kvh], 0u, __ATOMIC_RELAXED,
+    __hip_atomic_store(&p.counters[((size_t)seq * p.n_kv_heads + kvh) * kCounterStride], 0u, __ATOMIC_RELAXED,
                        __HIP_MEMORY_SCOPE_AGENT);
   }
 }
@@ -1608,44 +1608,61 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
 // by its own CU's bandwidth (hundreds of KB for 32-64 splits).  There the
 // attention kernel only stores the partials, and this kernel combines them
 // with one 64-lane work-group per (sequence, kv head, row): lane s holds
-// split s's maximum and sum, the weights exp2(m_s - M) / sum_s exp2(m_s - M)
-// l_s go through LDS, and each lane combines D/64 columns of the row.
+// split s's maximum and sum and forms its weight exp2(m_s - M) / sum_s
+// exp2(m_s - M) l_s, which the lanes read back one split at a time
+// (readlane), and each lane combines D/64 columns of the row in split order.
 template <int D>
 __device__ __forceinline__ void split_merge_body(const AttnParams& p, int blk) {
-  constexpr int C = D / 64;   // columns per lane
-  __shared__ float s_w[kMaxSplits];
+  constexpr int C = D / 64;      // columns per lane
+  constexpr int kPre = 32;       // splits whose partials are loaded up front
   const int lane = threadIdx.x;
   const int R = p.rows, G = p.group;
   const int r = blk % R;
   const int grp = blk / R;   // sequence * n_kv_heads + kv head
   const int seq = grp / p.n_kv_heads, kvh = grp - seq * p.n_kv_heads;
+  // Every slot of the group's partials (n_split of them) lies inside the
+  // workspace, so the maxima, sums and the first kPre partial rows are all
+  // loaded before the length says how many splits ran: one memory round
+  // trip.  Slots past that count hold stale values and are never used.
+  const size_t pbase = (size_t)grp * p.n_split;
+  const int nmax = min(p.n_split, kPre);
+  float2 ml = {-INFINITY, 0.0f};
+  if (lane < p.n_split) ml = *reinterpret_cast<const float2*>(p.part_ml + ((pbase + lane) * R + r) * 2);
+  const float* ob = p.part_o + (pbase * R + r) * D + C * lane;
+  float v[kPre][C];
+#pragma unroll
+  for (int k = 0; k < kPre; ++k) {
+    if (k < nmax) {
+#pragma unroll
+      for (int c = 0; c < C; ++c) v[k][c] = ob[(size_t)k * R * D + c];
+    }
+  }
   const int L = p.seq_len[seq];
   // (seq_len above max_seq_len breaks the call's contract; the clamp keeps
   // the reads inside this group's partials even then)
   const int nsp = min((L + p.chunk - 1) / p.chunk, p.n_split);
   if (nsp <= 1) return;   // a single split wrote its rows itself
-  const size_t pbase = (size_t)grp * p.n_split;
-  float m = -INFINITY, l = 0.0f;
-  if (lane < nsp) {
-    const float2 ml = *reinterpret_cast<const float2*>(p.part_ml + ((pbase + lane) * R + r) * 2);
-    m = ml.x;
-    l = ml.y;
-  }
+  const float m = lane < nsp ? ml.x : -INFINITY;
   const float M = wave_max(m);
   const float e = lane < nsp ? __builtin_amdgcn_exp2f(m - M) : 0.0f;
-  const float den = wave_sum(e * l);
-  if (lane < nsp) s_w[lane] = e / den;
-  __syncthreads();
-  const float* ob = p.part_o + (pbase * R + r) * D + C * lane;
+  const float den = wave_sum(e * (lane < nsp ? ml.y : 0.0f));
+  const float w = e / den;
   float acc[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) acc[c] = 0.0f;
-#pragma unroll 8
-  for (int sp = 0; sp < nsp; ++sp) {
-    const float w = s_w[sp];
-    const float* src = ob + (size_t)sp * R * D;
 #pragma unroll
-    for (int c = 0; c < C; ++c) acc[c] = fmaf(w, src[c], acc[c]);
+  for (int k = 0; k < kPre; ++k) {
+    if (k < nsp) {
+      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+#pragma unroll
+      for (int c = 0; c < C; ++c) acc[c] = fmaf(wk, v[k][c], acc[c]);
+    }
+  }
+  // more than kPre splits: the rest one by one
+  for (int k = kPre; k < nsp; ++k) {
+    const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+#pragma unroll
+    for (int c = 0; c < C; ++c) acc[c] = fmaf(wk, ob[(size_t)k * R * D + c], acc[c]);
   }
   float* dst = p.out + (((size_t)seq * p.n_qtok + r / G) * p.n_q_heads + kvh * G + r % G) * D + C * lane;
 #pragma unroll

@@ -29,6 +29,10 @@ struct WorkspaceLayout {
 constexpr int kTileTokens = 32;    // tokens per tile: split points fall on tile boundaries
 constexpr int kChunkAlign = 256;   // one 32-token tile for each of the 8 waves of a work-group
 constexpr int kMaxSplits = 64;     // splits per (sequence, kv head) the merge stages in LDS
+// uint32 words from one split counter to the next: each (sequence, kv head)
+// counter sits on its own 256-byte span, so that the work-groups of different
+// groups finishing at the same moment do not queue on one line's atomics
+constexpr int kCounterStride = 64;
 
 SplitPlan plan_splits(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads, int max_seq_len);
 WorkspaceLayout workspace_layout(const kvq_cache& c, int n_seq, int n_qtok, int n_q_heads,

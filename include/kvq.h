@@ -125,7 +125,8 @@ int kv_append_quant(const kvq_cache* cache, const float* k_new, const float* v_n
 /*
  * Workspace bytes attn_decode_packed needs for this shape (host only).  The
  * workspace is caller-owned device memory holding per-split softmax partials
- * and one split counter per (sequence, kv head).  It must be zero-filled
+ * and one split counter per (sequence, kv head), each on its own 256 bytes
+ * at the front.  It must be zero-filled
  * before its first use; every completed call leaves the counters at zero, so
  * it can be reused by later calls on the same stream without clearing.
  * Calls that overlap in time must use different workspaces.

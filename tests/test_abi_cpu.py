@@ -112,14 +112,14 @@ def _r256(x):
 
 def _splits_from_workspace(c, n_seq, n_qtok, hq, max_len):
     """The split count the planner chose, read back from the workspace size
-    (counters, then [groups][splits][rows][D] partial rows, then their (m, l))."""
+    (256-byte counters, then [groups][splits][rows][D] partial rows, then their (m, l))."""
     out = ctypes.c_size_t(0)
     assert K.lib().attn_decode_packed_workspace_size(ctypes.byref(c), n_seq, n_qtok, hq, max_len,
                                                       ctypes.byref(out)) == 0
     groups = n_seq * c.n_kv_heads
     rows = n_qtok * (hq // c.n_kv_heads)
     hits = [s for s in range(1, 65)
-            if _r256(groups * 4) + _r256(groups * s * rows * c.head_dim * 4) + _r256(groups * s * rows * 8)
+            if _r256(groups * 256) + _r256(groups * s * rows * c.head_dim * 4) + _r256(groups * s * rows * 8)
             == out.value]
     assert len(hits) == 1, (out.value, hits)
     return hits[0]

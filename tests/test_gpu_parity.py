@@ -328,7 +328,7 @@ def test_workspace_reuse_across_shapes():
         torch.cuda.synchronize()
         if L == 4096:
             H.assert_close(out.cpu().numpy(), ref_full, f"reuse L={L}")
-    counters = ws[:4 * 8].cpu().numpy().view(np.uint32)
+    counters = ws[:256 * 8].cpu().numpy().view(np.uint32)   # one per 256 bytes, the rest unused
     assert not counters.any()
 
 
@@ -358,7 +358,7 @@ def test_workspace_reuse_changing_inputs_odd_groups():
         K.attn_decode_packed(cache, q, out, sl, L, spec.sm_scale, False, ws)
         torch.cuda.synchronize()
         H.assert_close(out.cpu().numpy(), H.oracle_attention(ci), f"odd groups call {call}")
-    assert not ws[:4 * Hkv].cpu().numpy().any()
+    assert not ws[:256 * Hkv].cpu().numpy().any()
 
 
 def test_attention_errors_leave_output_untouched():
