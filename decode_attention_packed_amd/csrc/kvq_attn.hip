@@ -825,13 +825,26 @@ __device__ __forceinline__ uint32_t round_f16_pair(float p0, float p1, uint32_t 
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// One wave's merge block: its unnormalized rows ([16][DP] floats, rows
+// padded to DP >= D so that the writes spread over the LDS banks), then
+// their maxima and sums ([16] each).  A wave writes its block into its own
+// ring slots as soon as its ring ends (its loads have all landed and no
+// other wave reads those slots), so the waves meet at a single barrier.
+template <int D, int DP>
+struct MergeBlock {
+  static constexpr int FLOATS = kRows * DP + 2 * kRows;
+  __device__ static float* at(uint8_t* s_lds, int wave, int wave_bytes) {
+    return reinterpret_cast<float*>(s_lds + wave * wave_bytes);
+  }
+};
+
 // Publish this work-group's partial and, in the last work-group of the
 // (sequence, kv head), merge every split into the output rows.  On entry
-// s_buf holds each wave's unnormalized rows ([wave][16][D]) followed by their
-// maxima and sums ([wave][16] each), and the work-group is synchronized.  A
-// sequence with a single split writes its rows directly.
-template <int D, int LDS_BYTES>
-__device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, int* s_last, int seq,
+// every wave's merge block (MergeBlock<D, DP>, wave w's at s_lds + w *
+// WAVE_BYTES) is written and the work-group is synchronized.  A sequence
+// with a single split writes its rows directly.
+template <int D, int LDS_BYTES, int WAVE_BYTES, int DP>
+__device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds, int* s_last, int seq,
                                              int kvh, int split, int n_split_seq, bool off_xcd,
                                              unsigned long long* ts = nullptr) {
   constexpr int kBatch = 16;                              // partial loads in flight per thread
@@ -839,10 +852,11 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, 
                 "split merge does not fit the LDS buffer");
   // (the fp16-K build runs the column layout only: at most 4 rows)
   static_assert(kF16K || kRows * D / 4 <= kThreads, "one thread per output column at least");
+  static_assert(MergeBlock<D, DP>::FLOATS * 4 <= WAVE_BYTES, "a merge block does not fit a wave's slots");
+  using MB = MergeBlock<D, DP>;
   const int tid = threadIdx.x;
   const int R = p.rows, G = p.group;
-  float* s_m = s_buf + kWaves * kRows * D;
-  float* s_l = s_m + kWaves * kRows;
+  float* s_buf = reinterpret_cast<float*>(s_lds);
   auto out_row = [&](int r) {
     return p.out + (((size_t)seq * p.n_qtok + r / G) * p.n_q_heads + kvh * G + r % G) * D;
   };
@@ -855,15 +869,16 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, float* s_buf, 
   const size_t pbase = ((size_t)seq * p.n_kv_heads + kvh) * p.n_split;
   for (int e = tid; e < R * D; e += kThreads) {
     const int r = e / D;
-    float M = s_m[r];
+    float M = MB::at(s_lds, 0, WAVE_BYTES)[kRows * DP + r];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, s_m[w * kRows + r]);
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, MB::at(s_lds, w, WAVE_BYTES)[kRows * DP + r]);
     float o = 0.0f, l = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float a = __builtin_amdgcn_exp2f(s_m[w * kRows + r] - M);
-      o = fmaf(a, s_buf[(w * kRows + r) * D + (e - r * D)], o);
-      l = fmaf(a, s_l[w * kRows + r], l);
+      const float* mb = MB::at(s_lds, w, WAVE_BYTES);
+      const float a = __builtin_amdgcn_exp2f(mb[kRows * DP + r] - M);
+      o = fmaf(a, mb[r * DP + (e - r * D)], o);
+      l = fmaf(a, mb[kRows * DP + kRows + r], l);
     }
     if (single) {
       out_row(r)[e - r * D] = o / l;
@@ -1188,9 +1203,9 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   constexpr int NB = D / kBlock;
   constexpr int NT = D / 16;
   constexpr int RING = kWaves * S::NSLOT * S::BYTES + S::PBUF;
-  constexpr int MERGE = kWaves * kRows * D * 4 + 2 * kWaves * kRows * 4;
-  static_assert(MERGE <= RING, "the merge buffer overlaps the patch buffer");
   constexpr int LDS_BYTES = RING + S::PATCH;
+  constexpr int WAVE_BYTES = S::NSLOT * S::BYTES;   // one wave's ring slots, later its merge block
+  constexpr int DP = D + 4;                         // merge rows: a lane's 4 rows on distinct banks
 
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   __shared__ int s_last;
@@ -1204,7 +1219,7 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   const TileLane<D, VF> tl = tile_lane_offsets<D, VF>(lane);
   TileCursor cur = {-1, 0};
   TileQueue tq;
-  const uint32_t ring_lds = lds_addr(s_lds + wave * S::NSLOT * S::BYTES);
+  const uint32_t ring_lds = lds_addr(s_lds + wave * WAVE_BYTES);
   int8_t* s_qc;
   float* s_qd;
   uint8_t* s_patch = s_lds + RING;
@@ -1273,30 +1288,30 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
     if (lane == 0) s_ring_end[wave] = now_stamp();
   }
 
-  // ---- this wave's rows to LDS for the merge
-  float* s_buf = reinterpret_cast<float*>(s_lds);
-  float* s_m = s_buf + kWaves * kRows * D;
-  float* s_l = s_m + kWaves * kRows;
+  // ---- this wave's rows into its merge block (its own ring slots)
 #pragma unroll
   for (int i = 0; i < 4; ++i) st.lrow[i] = sum_row16(st.lrow[i]);
-  __syncthreads();   // every wave is done with its ring
+  {
+    float* mb = MergeBlock<D, DP>::at(s_lds, wave, WAVE_BYTES);
 #pragma unroll
-  for (int n = 0; n < NT; ++n) {
-    // q4_0: the high-nibble dims (odd n) accumulated 16 x their value
-    const float sc = (VF == 0 && (n & 1)) ? 0.0625f : 1.0f;
+    for (int n = 0; n < NT; ++n) {
+      // q4_0: the high-nibble dims (odd n) accumulated 16 x their value
+      const float sc = (VF == 0 && (n & 1)) ? 0.0625f : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_buf[(wave * kRows + 4 * grp + i) * D + 16 * n + col] = st.acc[n][i] * sc;
-  }
-  if (col == 0) {
+      for (int i = 0; i < 4; ++i) mb[(4 * grp + i) * DP + 16 * n + col] = st.acc[n][i] * sc;
+    }
+    if (col == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s_m[wave * kRows + 4 * grp + i] = st.mrow[i];
-      s_l[wave * kRows + 4 * grp + i] = st.lrow[i];
+      for (int i = 0; i < 4; ++i) {
+        mb[kRows * DP + 4 * grp + i] = st.mrow[i];
+        mb[kRows * DP + kRows + 4 * grp + i] = st.lrow[i];
+      }
     }
   }
-  __syncthreads();
+  __syncthreads();   // every wave's merge block is written
   if constexpr (DBG == 2) ring_end_stamps(s_ring_end, ts);
-  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq, ws.off_xcd, ts);
+  finish_split<D, LDS_BYTES, WAVE_BYTES, DP>(p, s_lds, &s_last, seq, kvh, split, n_split_seq, ws.off_xcd,
+                                             ts);
 }
 
 // ---------------------------------------------------------------------------
@@ -1482,9 +1497,9 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   constexpr int NB = D / kBlock;
   constexpr int NG = D / 16;
   constexpr int RING = kWaves * S::NSLOT * S::BYTES;
-  constexpr int MERGE = kWaves * kRows * D * 4 + 2 * kWaves * kRows * 4;
-  static_assert(MERGE <= RING, "the merge buffer overlaps the patch buffer");
   constexpr int LDS_BYTES = RING + S::PATCH;
+  constexpr int WAVE_BYTES = S::NSLOT * S::BYTES;   // one wave's ring slots, later its merge block
+  constexpr int DP = D + 16;                        // merge rows: 16-byte writes spread over all banks
 
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   __shared__ int s_last;
@@ -1498,7 +1513,7 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   const TileLane<D, VF> tl = tile_lane_offsets<D, VF>(lane);
   TileCursor cur = {-1, 0};
   TileQueue tq;
-  const uint32_t ring_lds = lds_addr(s_lds + wave * S::NSLOT * S::BYTES);
+  const uint32_t ring_lds = lds_addr(s_lds + wave * WAVE_BYTES);
   int8_t* s_qc;
   float* s_qd;
   uint8_t* s_patch = s_lds + RING;
@@ -1573,30 +1588,33 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
     if (lane == 0) s_ring_end[wave] = now_stamp();
   }
 
-  // ---- this wave's rows to LDS for the merge
-  float* s_buf = reinterpret_cast<float*>(s_lds);
-  float* s_m = s_buf + kWaves * kRows * D;
-  float* s_l = s_m + kWaves * kRows;
+  // ---- this wave's rows into its merge block (its own ring slots).  The
+  // lane's useful accumulators are the two of its block b (dims 32b +
+  // 4grp .. +4 and 32b + 16 + 4grp .. +4 of row r): picked by selects, then
+  // written with two 16-byte stores.
   const float l = across32(across16(st.l, fadd), fadd);
-  __syncthreads();   // every wave is done with its ring
   if (valid) {
-    // q4_0 high-nibble dims (odd g) were accumulated 16 times too large
+    // q4_0 high-nibble dims (odd groups) were accumulated 16 times too large
     constexpr float kHi = VF == 0 ? 0.0625f : 1.0f;
+    v4f lo = st.acc[0], hi = st.acc[1];
 #pragma unroll
-    for (int g = 0; g < NG; ++g)
-      if ((g >> 1) == b) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          s_buf[(wave * kRows + r) * D + 16 * g + 4 * grp + i] = (g & 1) ? st.acc[g][i] * kHi : st.acc[g][i];
-      }
+    for (int bb = 1; bb < NB; ++bb) {
+      lo = b == bb ? st.acc[2 * bb] : lo;
+      hi = b == bb ? st.acc[2 * bb + 1] : hi;
+    }
+    float* mb = MergeBlock<D, DP>::at(s_lds, wave, WAVE_BYTES);
+    float* dst = mb + r * DP + 32 * b + 4 * grp;
+    *reinterpret_cast<v4f*>(dst) = lo;
+    *reinterpret_cast<v4f*>(dst + 16) = hi * kHi;
     if (b == 0 && grp == 0) {
-      s_m[wave * kRows + r] = l > 0.0f ? st.m : -1e30f;
-      s_l[wave * kRows + r] = l;
+      mb[kRows * DP + r] = l > 0.0f ? st.m : -1e30f;
+      mb[kRows * DP + kRows + r] = l;
     }
   }
-  __syncthreads();
+  __syncthreads();   // every wave's merge block is written
   if constexpr (DBG == 2) ring_end_stamps(s_ring_end, ts);
-  finish_split<D, LDS_BYTES>(p, s_buf, &s_last, seq, kvh, split, n_split_seq, ws.off_xcd, ts);
+  finish_split<D, LDS_BYTES, WAVE_BYTES, DP>(p, s_lds, &s_last, seq, kvh, split, n_split_seq, ws.off_xcd,
+                                             ts);
 }
 
 // ---------------------------------------------------------------------------
