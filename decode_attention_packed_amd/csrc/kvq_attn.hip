@@ -1676,11 +1676,25 @@ __device__ __forceinline__ void split_merge_body(const AttnParams& p, int blk) {
       for (int c = 0; c < C; ++c) acc[c] = fmaf(wk, v[k][c], acc[c]);
     }
   }
-  // more than kPre splits: the rest one by one
-  for (int k = kPre; k < nsp; ++k) {
-    const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+  // more than kPre splits: the rest in batches of kPre, each batch's loads
+  // all in flight before its sums
+  for (int k0 = kPre; k0 < nsp; k0 += kPre) {
 #pragma unroll
-    for (int c = 0; c < C; ++c) acc[c] = fmaf(wk, ob[(size_t)k * R * D + c], acc[c]);
+    for (int k = 0; k < kPre; ++k) {
+      if (k0 + k < nsp) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) v[k][c] = ob[(size_t)(k0 + k) * R * D + c];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kPre; ++k) {
+      if (k0 + k < nsp) {
+        const float wk =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k0 + k));
+#pragma unroll
+        for (int c = 0; c < C; ++c) acc[c] = fmaf(wk, v[k][c], acc[c]);
+      }
+    }
   }
   float* dst = p.out + (((size_t)seq * p.n_qtok + r / G) * p.n_q_heads + kvh * G + r % G) * D + C * lane;
 #pragma unroll
