@@ -77,3 +77,36 @@ def test_noalloc_rejects_oversize_calls():
                                      0.1, True, seg_table=torch.zeros((1100, 1), dtype=torch.int32,
                                                                       device="cuda"))
     assert e.value.status == K.KVQ_ERR_WORKSPACE
+
+
+def test_noalloc_captured_in_a_graph():
+    """The entry point for callers that cannot allocate, captured once in a
+    graph (its counter fill is a kernel, not a memset) and replayed with new
+    Q each time, eager calls of the workspace entry point in between: every
+    replay equals the eager call on the same Q bit for bit."""
+    ci = W.make_inputs("gqa8k", ctx=4096)[0]
+    c = _case(ci)
+    spec = ci.spec
+    q = c["q"].clone()
+    out = torch.empty_like(q)
+    args = (c["cache"], q, out, c["sl"], c["mx"], spec.sm_scale, spec.causal)
+    # the first call on a device looks up the scratch array's address: outside the capture
+    K.attn_decode_packed_noalloc(*args, seg_table=c["table"])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side), torch.cuda.graph(graph, stream=side):
+        K.attn_decode_packed_noalloc(*args, seg_table=c["table"])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(4242)
+    for rep in range(4):
+        print(f"[gpu-test] noalloc graph replay {rep}", flush=True)
+        qn = (rng.standard_normal(tuple(q.shape)) * (1.0 + rep)).astype(np.float32)
+        q.copy_(torch.from_numpy(qn).cuda())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        want = _run(dict(c, q=q), noalloc=False)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), rep
