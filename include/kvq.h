@@ -164,11 +164,12 @@ int attn_decode_packed_workspace_size(const kvq_cache* cache, int n_seq, int n_q
  * q4_0, 8 for q8_0, cancelled by the normalization), which keeps small V
  * accurate (relative error at V scaled by 1e-3 as at unit scale) and
  * requires every cached V block's largest magnitude to be below 32000;
- * larger values overflow the fp16 operand (undefined output).  The split plan depends only on the shape arguments (n_seq,
- * n_qtok, n_q_heads, max_seq_len and the cache geometry; the environment
- * variable KVQ_CHUNK_TOKENS, a multiple of 256, overrides its split size for
- * tests); for a given plan the output bits are a pure function of the
- * inputs, identical from call to call.
+ * larger values overflow the fp16 operand (undefined output).
+ * The split plan depends only on the shape arguments (n_seq, n_qtok,
+ * n_q_heads, max_seq_len and the cache geometry; the environment variable
+ * KVQ_CHUNK_TOKENS, a multiple of 256, overrides its split size for tests);
+ * for a given plan the output bits are a pure function of the inputs,
+ * identical from call to call.
  */
 int attn_decode_packed(const kvq_cache* cache, const float* q, float* out, int n_seq,
                        int n_qtok, int n_q_heads, const int32_t* seg_table, int max_segs,
