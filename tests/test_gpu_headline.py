@@ -10,8 +10,9 @@
 * The 12-wave column kernel (q4_0 V, head_dim 128, chunks of at least 1536
   tokens) against the oracle on all 32 query heads, plain and with the
   fused append, at 65536 tokens, at the 131073-token plan (chunks of 4128
-  tokens, a short last split, a partial tile), and at lengths that are not
-  whole tiles under forced chunk sizes.
+  tokens, a short last split, a partial tile), at lengths that are not
+  whole tiles under forced chunk sizes, and at 262144 tokens (8192-token
+  chunks, sampled heads).
 """
 import numpy as np
 import pytest
@@ -184,3 +185,17 @@ def test_timeline_hook(name, ctx):
     merged = live & ((T[..., 7] & 3) != 0)
     assert np.array_equal(merged.sum(axis=2), np.ones(merged.shape[:2], int)) or spec.n_qtok * (
         spec.n_q_heads // spec.n_kv_heads) * (spec.head_dim // 32) > 16   # row layout: merge launch
+
+
+def test_w12_262144_tokens_sampled_heads():
+    """Twice the 128k context: the planner cuts 262144 tokens into 32 splits
+    of 8192 (256 tiles per work-group, 21-22 per wave), the longest chunks
+    the column kernel runs at this head count; the long-context recipe,
+    seven of the 32 query heads (spread over five kv heads) against the
+    oracle."""
+    ci = W.make_inputs("long128k", ctx=262144)[0]
+    _say("w12 262144 tokens")
+    cache, table, max_segs = H.build_cache(ci)
+    heads = [0, 5, 9, 14, 19, 27, 31]
+    got = H.run_attention(cache, ci, table, max_segs)
+    H.assert_close(got, H.oracle_attention(ci, q_heads=heads), "w12 262144 sampled heads")
