@@ -862,35 +862,43 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
   };
 
   // ---- merge the waves: one (m, l, o) per row
+  // A wave takes 64 consecutive elements of one row (D is a multiple of 64),
+  // so the row's per-wave weights are one exponential in each of the first
+  // kWaves lanes, broadcast with readlane; every lane then folds the waves'
+  // partial values in wave order.
   // Partials go out with agent-scope stores (write-through, coherent across
   // XCDs once complete), so publishing needs only a wait for the stores and
   // the counter increment, not a write-back of the whole L2.
+  static_assert(D % 64 == 0 && kWaves <= 16, "one row per wave, the waves' weights in one DPP row");
   const bool single = n_split_seq == 1;
   const size_t pbase = ((size_t)seq * p.n_kv_heads + kvh) * p.n_split;
-  for (int e = tid; e < R * D; e += kThreads) {
-    const int r = e / D;
-    float M = MB::at(s_lds, 0, WAVE_BYTES)[kRows * DP + r];
+  float* const po = p.part_o + ((pbase + split) * R) * D;      // this split's rows
+  float* const pml = p.part_ml + ((pbase + split) * R) * 2;
+  {
+    const int lane = tid & 63;
+    for (int e0 = __builtin_amdgcn_readfirstlane(tid - lane); e0 < R * D; e0 += kThreads) {
+      const int r = e0 / D;
+      const int d = e0 - r * D + lane;
+      const float mw = lane < kWaves ? MB::at(s_lds, lane, WAVE_BYTES)[kRows * DP + r] : -INFINITY;
+      const float lw = lane < kWaves ? MB::at(s_lds, lane, WAVE_BYTES)[kRows * DP + kRows + r] : 0.0f;
+      const float M = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, max_row16(mw)), 0));
+      const float a = __builtin_amdgcn_exp2f(mw - M);             // wave `lane`'s weight (0 past kWaves)
+      const float l = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sum_row16(a * lw)), 0));
+      float o = 0.0f;
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, MB::at(s_lds, w, WAVE_BYTES)[kRows * DP + r]);
-    float o = 0.0f, l = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      const float* mb = MB::at(s_lds, w, WAVE_BYTES);
-      const float a = __builtin_amdgcn_exp2f(mb[kRows * DP + r] - M);
-      o = fmaf(a, mb[r * DP + (e - r * D)], o);
-      l = fmaf(a, mb[kRows * DP + kRows + r], l);
-    }
-    if (single) {
-      out_row(r)[e - r * D] = o / l;
-      continue;
-    }
-    __hip_atomic_store(&p.part_o[((pbase + split) * R) * D + e], o, __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    if (e - r * D == 0) {
-      __hip_atomic_store(&p.part_ml[((pbase + split) * R + r) * 2], M, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&p.part_ml[((pbase + split) * R + r) * 2 + 1], l, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
+      for (int w = 0; w < kWaves; ++w) {
+        const float aw = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, a), w));
+        o = fmaf(aw, MB::at(s_lds, w, WAVE_BYTES)[r * DP + d], o);
+      }
+      if (single) {
+        out_row(r)[d] = o / l;
+        continue;
+      }
+      __hip_atomic_store(po + r * D + d, o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (d == 0) {
+        __hip_atomic_store(pml + 2 * r, M, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(pml + 2 * r + 1, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
   // with the merge as its own launch, the kernel boundary publishes the partials
@@ -910,7 +918,14 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
     const unsigned done = __hip_atomic_fetch_add(&p.counters[((size_t)seq * p.n_kv_heads + kvh) * kCounterStride], inc,
                                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = (done & 0xFFFFu) == (unsigned)(n_split_seq - 1);
-    *s_last = last ? (((done + inc) >> 16) == 0 ? 2 : 1) : 0;
+    const int code = last ? (((done + inc) >> 16) == 0 ? 2 : 1) : 0;
+    // The last group of this (sequence, kv head) merges the partials of
+    // every split.  When every split ran on this XCD, their stores went
+    // through this L2 and only the CU's own cache needs dropping: done here,
+    // once for all waves (they load only after the barrier below), not by
+    // each wave.
+    if (code == 2) asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory");
+    *s_last = code;
     if (ts) {
       ts[kStPub] = now_stamp();
       ts[kStFlags] = last ? 1u : 0u;
@@ -918,15 +933,8 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
   }
   __syncthreads();
   if (!*s_last) return;
-  // The last group of this (sequence, kv head) merges the partials of every
-  // split.  When every split ran on this XCD, their stores went through this
-  // L2 and only the CU's own cache needs dropping; otherwise stale lines of
-  // the whole L2 are dropped first.
-  if (*s_last == 2) {
-    asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory");
-  } else {
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  }
+  // Some split ran on another XCD: stale lines of the whole L2 are dropped.
+  if (*s_last == 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   static_assert(kMaxSplits <= 64, "one lane per split");
   const int nsp = n_split_seq;
   float* sw = s_buf;                                    // [nsp][R] split weights
@@ -936,9 +944,26 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
   const int c = tid % cols, part = tid / cols;
   const bool active = part < tpc;
   const int r = (4 * c) / D;
-  const float* ob = p.part_o + (pbase * R) * D + 4 * c;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Thread (part, c) adds float4 column c of splits part, part + tpc, ...:
+  // batch k of every part is split part + tpc * k, so a batch's loads are a
+  // uniform base plus the thread's fixed byte offset, with no per-load
+  // address arithmetic.  Every part has a split in the first nfull batches
+  // and the parts below rem in one more; in that last batch the other parts
+  // load split nsp - 1 again with weight 0 (a finite partial, so the sum is
+  // unchanged), which keeps every load and add free of lane masks.  Threads
+  // beyond the last part do part 0's work and never store it.
+  const int nfull = nsp / tpc, rem = nsp - nfull * tpc;
+  const int nb = nfull + (rem > 0 ? 1 : 0);              // batches
+  const int bstride = tpc * R * D;                       // floats from one batch to the next
+  const float* const ob = p.part_o + (pbase * R) * D;
+  const int pa = active ? part : 0;
+  const bool extra = pa < rem;
+  const int px = extra ? pa : rem - 1;                   // the part loaded in the last batch
+  const uint32_t boff = (uint32_t)((pa * R * D + 4 * c) * 4);
+  const uint32_t boffx = (uint32_t)((px * R * D + 4 * c) * 4);
+  const int wo = pa * R + r, wox = px * R + r;           // the thread's split weights: sw[split * R + r]
 
   // split maxima and sums first (wave w takes rows w, w + kWaves, one lane
   // per split), then the first batch of partial outputs, all in flight at once
@@ -952,11 +977,16 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
       ml[k] = *reinterpret_cast<const float2*>(p.part_ml + ((pbase + lane) * R + rr) * 2);
   }
   float4 v[kBatch];
+  auto load_batch = [&](int k0) {
+    const char* pk = reinterpret_cast<const char*>(ob + (size_t)k0 * bstride);   // uniform
 #pragma unroll
-  for (int k = 0; k < kBatch; ++k) {
-    const int sp = part + tpc * k;
-    if (active && sp < nsp) v[k] = *reinterpret_cast<const float4*>(ob + (size_t)sp * R * D);
-  }
+    for (int k = 0; k < kBatch; ++k) {
+      if (k0 + k >= nb) break;
+      v[k] = *reinterpret_cast<const float4*>(pk + (k0 + k < nfull ? boff : boffx));
+      pk += (size_t)bstride * 4;
+    }
+  };
+  load_batch(0);
   // weights exp2(m_s - M) / sum_s exp2(m_s - M) l_s
 #pragma unroll
   for (int k = 0; k < kRowsPerWave; ++k) {
@@ -970,29 +1000,31 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
   __syncthreads();
 
   float4 a = {0.0f, 0.0f, 0.0f, 0.0f};
-  auto add = [&](float w, const float4& x) {
-    a.x = fmaf(w, x.x, a.x);
-    a.y = fmaf(w, x.y, a.y);
-    a.z = fmaf(w, x.z, a.z);
-    a.w = fmaf(w, x.w, a.w);
+  auto add_batch = [&](int k0) {
+    float w[kBatch];
+    const float* swk = sw + k0 * tpc * R;                 // uniform
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (k0 + k >= nb) break;
+      const bool full = k0 + k < nfull;
+      const float x = swk[full ? wo : wox];
+      w[k] = full || extra ? x : 0.0f;
+      swk += tpc * R;
+    }
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (k0 + k >= nb) break;
+      a.x = fmaf(w[k], v[k].x, a.x);
+      a.y = fmaf(w[k], v[k].y, a.y);
+      a.z = fmaf(w[k], v[k].z, a.z);
+      a.w = fmaf(w[k], v[k].w, a.w);
+    }
   };
-#pragma unroll
-  for (int k = 0; k < kBatch; ++k) {
-    const int sp = part + tpc * k;
-    if (active && sp < nsp) add(sw[sp * R + r], v[k]);
-  }
+  add_batch(0);
   // more splits than one batch covers (large row groups): further batches
-  for (int sp0 = part + tpc * kBatch; active && sp0 < nsp; sp0 += tpc * kBatch) {
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int sp = sp0 + tpc * k;
-      if (sp < nsp) v[k] = *reinterpret_cast<const float4*>(ob + (size_t)sp * R * D);
-    }
-#pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
-      const int sp = sp0 + tpc * k;
-      if (sp < nsp) add(sw[sp * R + r], v[k]);
-    }
+  for (int k0 = kBatch; k0 < nb; k0 += kBatch) {
+    load_batch(k0);
+    add_batch(k0);
   }
   if (active) red[part * cols + c] = a;
   __syncthreads();
