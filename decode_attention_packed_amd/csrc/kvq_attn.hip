@@ -909,36 +909,11 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
     }
     return;
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  // The counter's low 16 bits count finished splits; each work-group that is
-  // not on its group's XCD also adds 1 << 16.
-  if (tid == 0) {
-    const unsigned inc = 1u + (off_xcd ? (1u << 16) : 0u);
-    const unsigned done = __hip_atomic_fetch_add(&p.counters[((size_t)seq * p.n_kv_heads + kvh) * kCounterStride], inc,
-                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = (done & 0xFFFFu) == (unsigned)(n_split_seq - 1);
-    const int code = last ? (((done + inc) >> 16) == 0 ? 2 : 1) : 0;
-    // The last group of this (sequence, kv head) merges the partials of
-    // every split.  When every split ran on this XCD, their stores went
-    // through this L2 and only the CU's own cache needs dropping: done here,
-    // once for all waves (they load only after the barrier below), not by
-    // each wave.
-    if (code == 2) asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory");
-    *s_last = code;
-    if (ts) {
-      ts[kStPub] = now_stamp();
-      ts[kStFlags] = last ? 1u : 0u;
-    }
-  }
-  __syncthreads();
-  if (!*s_last) return;
-  // Some split ran on another XCD: stale lines of the whole L2 are dropped.
-  if (*s_last == 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // The split merge's addressing, formed by every work-group while its
+  // partial's stores are being acknowledged (off the merging work-group's
+  // critical path).
   static_assert(kMaxSplits <= 64, "one lane per split");
   const int nsp = n_split_seq;
-  float* sw = s_buf;                                    // [nsp][R] split weights
-  float4* red = reinterpret_cast<float4*>(sw + kMaxSplits * kRows);   // [tpc][cols]
   const int cols = R * D / 4;              // float4 columns of the output rows
   const int tpc = kThreads / cols;         // threads per column
   const int c = tid % cols, part = tid / cols;
@@ -965,6 +940,38 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
   const uint32_t boffx = (uint32_t)((px * R * D + 4 * c) * 4);
   const int wo = pa * R + r, wox = px * R + r;           // the thread's split weights: sw[split * R + r]
 
+  const float* const pmlw = p.part_ml + ((pbase + lane) * R + wave) * 2;   // row `wave`, split `lane`
+  const int rd = (4 * tid) / D;                          // the row of output column tid
+  float* const dst = out_row(rd < R ? rd : 0) + (4 * tid - rd * D);
+  asm volatile("" ::"v"(boff), "v"(boffx), "v"(wo), "v"(wox), "v"(pmlw), "v"(dst), "s"(nfull), "s"(nb), "s"(tpc));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  // The counter's low 16 bits count finished splits; each work-group that is
+  // not on its group's XCD also adds 1 << 16.
+  if (tid == 0) {
+    const unsigned inc = 1u + (off_xcd ? (1u << 16) : 0u);
+    const unsigned done = __hip_atomic_fetch_add(&p.counters[((size_t)seq * p.n_kv_heads + kvh) * kCounterStride], inc,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = (done & 0xFFFFu) == (unsigned)(n_split_seq - 1);
+    const int code = last ? (((done + inc) >> 16) == 0 ? 2 : 1) : 0;
+    // The last group of this (sequence, kv head) merges the partials of
+    // every split.  When every split ran on this XCD, their stores went
+    // through this L2 and only the CU's own cache needs dropping: done here,
+    // once for all waves (they load only after the barrier below), not by
+    // each wave.
+    if (code == 2) asm volatile("buffer_inv sc0\n\ts_waitcnt vmcnt(0)" ::: "memory");
+    *s_last = code;
+    if (ts) {
+      ts[kStPub] = now_stamp();
+      ts[kStFlags] = last ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  if (!*s_last) return;
+  // Some split ran on another XCD: stale lines of the whole L2 are dropped.
+  if (*s_last == 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  float* sw = s_buf;                                    // [nsp][R] split weights
+  float4* red = reinterpret_cast<float4*>(sw + kMaxSplits * kRows);   // [tpc][cols]
   // split maxima and sums first (wave w takes rows w, w + kWaves, one lane
   // per split), then the first batch of partial outputs, all in flight at once
   constexpr int kRowsPerWave = (kRows + kWaves - 1) / kWaves;
@@ -974,7 +981,7 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
     const int rr = wave + kWaves * k;
     ml[k] = (float2){-INFINITY, 0.0f};
     if (rr < R && lane < nsp)
-      ml[k] = *reinterpret_cast<const float2*>(p.part_ml + ((pbase + lane) * R + rr) * 2);
+      ml[k] = *reinterpret_cast<const float2*>(pmlw + 2 * kWaves * k);
   }
   float4 v[kBatch];
   auto load_batch = [&](int k0) {
@@ -1037,8 +1044,7 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
       o.z += b.z;
       o.w += b.w;
     }
-    const int rr = (4 * cc) / D;
-    *reinterpret_cast<float4*>(out_row(rr) + (4 * cc - rr * D)) = o;
+    *reinterpret_cast<float4*>(cc == tid ? dst : out_row((4 * cc) / D) + (4 * cc - ((4 * cc) / D) * D)) = o;
   }
   if (tid == 0) {
     if (ts) ts[kStDone] = now_stamp();
