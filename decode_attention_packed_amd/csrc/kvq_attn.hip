@@ -939,8 +939,8 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
   // address arithmetic.  Every part has a split in the first nfull batches
   // and the parts below rem in one more; in that last batch the other parts
   // load split nsp - 1 again with weight 0 (a finite partial, so the sum is
-  // unchanged), which keeps every load and add free of lane masks.  Waves
-  // past the last part load nothing.
+  // unchanged), which keeps every load and add free of lane masks.  Threads
+  // past the last part (tid >= tpc * cols) load and add nothing.
   const int nfull = nsp / tpc, rem = nsp - nfull * tpc;
   const int nb = nfull + (rem > 0 ? 1 : 0);              // batches
   const int bstride = tpc * R * D;                       // floats from one batch to the next
@@ -1005,7 +1005,7 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
       pk += (size_t)bstride * 4;
     }
   };
-  if (active) load_batch(0);   // whole waves are active or idle (tpc * cols is a multiple of 64)
+  if (active) load_batch(0);
   // weights exp2(m_s - M) / sum_s exp2(m_s - M) l_s
 #pragma unroll
   for (int k = 0; k < kRowsPerWave; ++k) {
