@@ -126,13 +126,15 @@ struct AttnParams {
 };
 
 // The timeline mode's stamps, per work-group ([sequence][kv head][split, up
-// to kMaxSplits][kStamps]), in the device's constant
-// 100 MHz clock (s_memrealtime): entry, Q codes ready (after the prologue's
-// barrier), wave 0's first tile ready, the first and the last wave's ring
-// done, partial published (split counter returned; stores issued for the
-// row layout, whose merge is a second launch), merge or direct output done,
-// and flags (bit 0: this work-group merged the splits, bit 1: a single split
-// wrote its rows directly).
+// to kMaxSplits][kStamps]), in the device's constant 100 MHz clock
+// (s_memrealtime): entry, Q codes ready (after the prologue's barrier), wave
+// 0's first tile ready, the first and the last wave's ring done, partial
+// published (split counter returned; stores issued for the row layout, whose
+// merge is a second launch), merge or direct output done, and flags (bit 0:
+// this work-group merged the splits, bit 1: a single split wrote its rows
+// directly).  They are kept in LDS while the work-group runs and written out
+// at its end: a stamp stored to memory mid-kernel would sit in the next wait
+// on the memory counter and lengthen the phase it measures.
 enum { kStStart, kStQ, kStTile, kStRing0, kStRing1, kStPub, kStDone, kStFlags, kStamps };
 __device__ __forceinline__ unsigned long long* stamp_row(const AttnParams& p, int seq, int kvh, int split) {
   return p.dbg_stamps + (((size_t)seq * p.n_kv_heads + kvh) * kMaxSplits + split) * kStamps;
@@ -1262,6 +1264,7 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   __shared__ int s_last;
   __shared__ unsigned long long s_ring_end[DBG == 2 ? kWaves : 1];
+  __shared__ unsigned long long s_tl[DBG == 2 ? kStamps : 1];   // this work-group's stamps
 
   const unsigned long long t_entry = DBG == 2 ? now_stamp() : 0ull;
   const int tid = threadIdx.x;
@@ -1283,10 +1286,11 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   const int R = p.rows, G = p.group;
   unsigned long long* ts = nullptr;
   if constexpr (DBG == 2) {
-    ts = stamp_row(p, seq, kvh, split);
+    ts = s_tl;
     if (tid == 0) {
-      ts[kStStart] = t_entry;
-      ts[kStQ] = now_stamp();
+      for (int k = 0; k < kStamps; ++k) s_tl[k] = 0;
+      s_tl[kStStart] = t_entry;
+      s_tl[kStQ] = now_stamp();
     }
   }
   bool first_tile = true;
@@ -1364,6 +1368,13 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   if constexpr (DBG == 2) ring_end_stamps(s_ring_end, ts);
   finish_split<D, LDS_BYTES, WAVE_BYTES, DP>(p, s_lds, &s_last, seq, kvh, split, n_split_seq, ws.off_xcd,
                                              ts);
+  if constexpr (DBG == 2) {
+    // every stamp was taken by thread 0, which copies them out last
+    if (tid == 0) {
+      unsigned long long* row = stamp_row(p, seq, kvh, split);
+      for (int k = 0; k < kStamps; ++k) row[k] = s_tl[k];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1556,6 +1567,7 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   __shared__ __attribute__((aligned(16))) uint8_t s_lds[LDS_BYTES];
   __shared__ int s_last;
   __shared__ unsigned long long s_ring_end[DBG == 2 ? kWaves : 1];
+  __shared__ unsigned long long s_tl[DBG == 2 ? kStamps : 1];   // this work-group's stamps
 
   const unsigned long long t_entry = DBG == 2 ? now_stamp() : 0ull;
   const int tid = threadIdx.x;
@@ -1577,10 +1589,11 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   const int R = p.rows, G = p.group;
   unsigned long long* ts = nullptr;
   if constexpr (DBG == 2) {
-    ts = stamp_row(p, seq, kvh, split);
+    ts = s_tl;
     if (tid == 0) {
-      ts[kStStart] = t_entry;
-      ts[kStQ] = now_stamp();
+      for (int k = 0; k < kStamps; ++k) s_tl[k] = 0;
+      s_tl[kStStart] = t_entry;
+      s_tl[kStQ] = now_stamp();
     }
   }
 
@@ -1667,6 +1680,13 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   if constexpr (DBG == 2) ring_end_stamps(s_ring_end, ts);
   finish_split<D, LDS_BYTES, WAVE_BYTES, DP>(p, s_lds, &s_last, seq, kvh, split, n_split_seq, ws.off_xcd,
                                              ts);
+  if constexpr (DBG == 2) {
+    // every stamp was taken by thread 0, which copies them out last
+    if (tid == 0) {
+      unsigned long long* row = stamp_row(p, seq, kvh, split);
+      for (int k = 0; k < kStamps; ++k) row[k] = s_tl[k];
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------

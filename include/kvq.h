@@ -353,7 +353,9 @@ int kvq_debug_attn_isum(const kvq_cache* cache, const float* q, float* out, int 
  *           published (split counter returned; stores issued when the merge
  *           is a second launch), 6 merge or direct output done, 7 flags
  *           (bit 0: this work-group merged the splits, bit 1: a single split
- *           wrote its rows directly).  Work-groups past a sequence's end
+ *           wrote its rows directly); entries a work-group never reached are
+ *           0.  A work-group writes its 8 entries once, at its end (it keeps
+ *           them on chip meanwhile).  Work-groups past a sequence's end
  *           write nothing.
  * Errors as attn_decode_packed; KVQ_ERR_INVALID for a NULL or misaligned
  * stamps buffer.
