@@ -103,6 +103,8 @@ struct AttnParams {
   int n_qtok;
   int group;
   int rows;               // n_qtok * group, at most 16
+  float rcp_group;        // 1 / group, for small_div
+  float rcp_cols;         // 1 / (rows * head_dim / 4), for small_div
   int seg_tokens;
   int max_segs;
   int chunk;              // tokens per work-group, a multiple of kTile
@@ -317,6 +319,13 @@ __device__ __forceinline__ int load_uniform(const int32_t* ptr) {
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// n / d (0 <= n < 2^20, d >= 1) from r = 1 / d as a float (correctly
+// rounded, or v_rcp_f32's 1 ulp): (n + 0.5) * r is off by at most
+// (n + 0.5) / d * 2^-22, below the 0.5 / d between (n + 0.5) / d and the
+// integers on either side, so the truncation gives floor(n / d) exactly.
+// Three VALU instructions in place of an integer division's ~20.
+__device__ __forceinline__ int small_div(int n, float r) { return (int)(((float)n + 0.5f) * r); }
 
 // K rows are stored in LDS with their 16-byte chunks permuted: chunk q of
 // token row t sits at chunk q ^ kswz(t) of the row.  The column layout reads
@@ -673,7 +682,8 @@ __device__ __forceinline__ int prologue_issue(const AttnParams& p, uint8_t* s_ld
       if (base + 64 <= PIECES || pc < PIECES) {
         const int r = wave + kWaves * (pc / (D / 4));
         const int rr = r < R ? r : 0;
-        const float* src = p.q + (((size_t)seq * p.n_qtok + rr / G) * p.n_q_heads + kvh * G + rr % G) * D +
+        const int tq = small_div(rr, p.rcp_group);
+        const float* src = p.q + (((size_t)seq * p.n_qtok + tq) * p.n_q_heads + kvh * G + rr - tq * G) * D +
                            4 * (pc % (D / 4));
         dma16_v(src, ring_lds + (NSLOT - 1) * S::BYTES + 16 * base);
       }
@@ -872,7 +882,8 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
   const int R = p.rows, G = p.group;
   float* s_buf = reinterpret_cast<float*>(s_lds);
   auto out_row = [&](int r) {
-    return p.out + (((size_t)seq * p.n_qtok + r / G) * p.n_q_heads + kvh * G + r % G) * D;
+    const int t = small_div(r, p.rcp_group);
+    return p.out + (((size_t)seq * p.n_qtok + t) * p.n_q_heads + kvh * G + r - t * G) * D;
   };
 
   // ---- merge the waves: one (m, l, o) per row
@@ -929,8 +940,8 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
   static_assert(kMaxSplits <= 64, "one lane per split");
   const int nsp = n_split_seq;
   const int cols = R * D / 4;              // float4 columns of the output rows
-  const int tpc = kThreads / cols;         // threads per column
-  const int c = tid % cols, part = tid / cols;
+  const int tpc = small_div(kThreads, p.rcp_cols);   // threads per column
+  const int part = small_div(tid, p.rcp_cols), c = tid - part * cols;
   const bool active = part < tpc;
   const int r = (4 * c) / D;
   const int lane = tid & 63;
@@ -943,7 +954,7 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
   // load split nsp - 1 again with weight 0 (a finite partial, so the sum is
   // unchanged), which keeps every load and add free of lane masks.  Threads
   // past the last part (tid >= tpc * cols) load and add nothing.
-  const int nfull = nsp / tpc, rem = nsp - nfull * tpc;
+  const int nfull = small_div(nsp, __builtin_amdgcn_rcpf((float)tpc)), rem = nsp - nfull * tpc;
   const int nb = nfull + (rem > 0 ? 1 : 0);              // batches
   const int bstride = tpc * R * D;                       // floats from one batch to the next
   const float* const ob = p.part_o + (pbase * R) * D;
@@ -1891,6 +1902,8 @@ static AttnParams make_params(const kvq_cache& c, const float* q, float* out, in
   p.n_split = plan.n_split;
   p.causal = causal;
   p.scale_log2 = sm_scale * 1.4426950408889634f;
+  p.rcp_group = 1.0f / (float)p.group;
+  p.rcp_cols = 4.0f / (float)(p.rows * c.head_dim);
   p.n_seq_groups = n_seq * c.n_kv_heads;
   // XCD-local placement when it costs no parallelism (see block_coords)
   p.xcd_local = p.n_seq_groups % kXcds == 0 || (long long)p.n_seq_groups * plan.n_split <= 64;
