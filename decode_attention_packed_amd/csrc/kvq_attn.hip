@@ -871,16 +871,15 @@ template <int D, int LDS_BYTES, int WAVE_BYTES, int DP>
 __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds, int* s_last, int seq,
                                              int kvh, int split, int n_split_seq, bool off_xcd,
                                              unsigned long long* ts = nullptr) {
-  constexpr int kBatch = 16;                              // partial loads in flight per thread
-  static_assert(kMaxSplits * kRows * 4 + 16 * kThreads <= LDS_BYTES,
-                "split merge does not fit the LDS buffer");
-  // (the fp16-K build runs the column layout only: at most 4 rows)
-  static_assert(kF16K || kRows * D / 4 <= kThreads, "one thread per output column at least");
+  constexpr int kBatch = 16;                              // partial loads in flight per lane
+  // The column layout (the only one merging here) has rows * D / 32 <= 16,
+  // so at most 8 rows (head_dim 64, 8-wave build) or 4 (head_dim 128): one
+  // wave per row.
+  static_assert(D == 128 || kWaves >= 8, "one wave per row of the column layout");
   static_assert(MergeBlock<D, DP>::FLOATS * 4 <= WAVE_BYTES, "a merge block does not fit a wave's slots");
   using MB = MergeBlock<D, DP>;
   const int tid = threadIdx.x;
   const int R = p.rows, G = p.group;
-  float* s_buf = reinterpret_cast<float*>(s_lds);
   auto out_row = [&](int r) {
     const int t = small_div(r, p.rcp_group);
     return p.out + (((size_t)seq * p.n_qtok + t) * p.n_q_heads + kvh * G + r - t * G) * D;
@@ -936,39 +935,29 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
   }
   // The split merge's addressing, formed by every work-group while its
   // partial's stores are being acknowledged (off the merging work-group's
-  // critical path).
+  // critical path).  Wave w merges output row w on its own (the column
+  // layout has at most kWaves rows): lane (g, c) adds float4 column c of
+  // splits g, g + SG, g + 2 SG, ..., so batch k's loads are a uniform base
+  // plus the lane's fixed offset; the SG lane groups are summed by lane
+  // swaps at the end, and no LDS or barrier is involved.  In the last batch
+  // the lanes without a split reload split nsp - 1 (a finite partial) with
+  // weight 0, which keeps the loads and adds free of lane masks.
   static_assert(kMaxSplits <= 64, "one lane per split");
+  constexpr int CR = D / 4;                              // float4 columns of a row
+  constexpr int SG = 64 / CR;                            // split groups per wave
   const int nsp = n_split_seq;
-  const int cols = R * D / 4;              // float4 columns of the output rows
-  const int tpc = small_div(kThreads, p.rcp_cols);   // threads per column
-  const int part = small_div(tid, p.rcp_cols), c = tid - part * cols;
-  const bool active = part < tpc;
-  const int r = (4 * c) / D;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  // Thread (part, c) adds float4 column c of splits part, part + tpc, ...:
-  // batch k of every part is split part + tpc * k, so a batch's loads are a
-  // uniform base plus the thread's fixed byte offset, with no per-load
-  // address arithmetic.  Every part has a split in the first nfull batches
-  // and the parts below rem in one more; in that last batch the other parts
-  // load split nsp - 1 again with weight 0 (a finite partial, so the sum is
-  // unchanged), which keeps every load and add free of lane masks.  Threads
-  // past the last part (tid >= tpc * cols) load and add nothing.
-  const int nfull = small_div(nsp, __builtin_amdgcn_rcpf((float)tpc)), rem = nsp - nfull * tpc;
-  const int nb = nfull + (rem > 0 ? 1 : 0);              // batches
-  const int bstride = tpc * R * D;                       // floats from one batch to the next
-  const float* const ob = p.part_o + (pbase * R) * D;
-  const int pa = active ? part : 0;
-  const bool extra = pa < rem;
-  const int px = extra ? pa : rem - 1;                   // the part loaded in the last batch
-  const uint32_t boff = (uint32_t)((pa * R * D + 4 * c) * 4);
-  const uint32_t boffx = (uint32_t)((px * R * D + 4 * c) * 4);
-  const int wo = pa * R + r, wox = px * R + r;           // the thread's split weights: sw[split * R + r]
-
-  const float* const pmlw = p.part_ml + ((pbase + lane) * R + wave) * 2;   // row `wave`, split `lane`
-  const int rd = (4 * tid) / D;                          // the row of output column tid
-  float* const dst = out_row(rd < R ? rd : 0) + (4 * tid - rd * D);
-  asm volatile("" ::"v"(boff), "v"(boffx), "v"(wo), "v"(wox), "v"(pmlw), "v"(dst), "s"(nfull), "s"(nb), "s"(tpc));
+  const int g = lane / CR, c = lane % CR;
+  const int nb = (nsp + SG - 1) / SG;                    // batches
+  const int gx = min(g, nsp - 1 - SG * (nb - 1));        // the split group loaded in the last batch
+  const int wr = wave < R ? wave : 0;
+  const float* const ob = p.part_o + (pbase * R + wr) * D;   // row wr of split 0
+  const uint32_t boff = (uint32_t)((g * R * D + 4 * c) * 4);
+  const uint32_t boffx = (uint32_t)((gx * R * D + 4 * c) * 4);
+  const float* const pmlw = p.part_ml + ((pbase + lane) * R + wr) * 2;   // split `lane`, row wr
+  float* const dst = out_row(wr) + 4 * c;
+  asm volatile("" ::"v"(boff), "v"(boffx), "v"(pmlw), "v"(dst), "s"(nb));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   // The counter's low 16 bits count finished splits; each work-group that is
@@ -995,84 +984,60 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
   if (!*s_last) return;
   // Some split ran on another XCD: stale lines of the whole L2 are dropped.
   if (*s_last == 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  float* sw = s_buf;                                    // [nsp][R] split weights
-  float4* red = reinterpret_cast<float4*>(sw + kMaxSplits * kRows);   // [tpc][cols]
-  // split maxima and sums first (wave w takes rows w, w + kWaves, one lane
-  // per split), then the first batch of partial outputs, all in flight at once
-  constexpr int kRowsPerWave = (kRows + kWaves - 1) / kWaves;
-  float2 ml[kRowsPerWave];
-#pragma unroll
-  for (int k = 0; k < kRowsPerWave; ++k) {
-    const int rr = wave + kWaves * k;
-    ml[k] = (float2){-INFINITY, 0.0f};
-    if (rr < R && lane < nsp)
-      ml[k] = *reinterpret_cast<const float2*>(pmlw + 2 * kWaves * k);
-  }
+  if (wave >= R) return;
+  // this row's split maxima and sums (lane = split), then the first batch of
+  // partial outputs, all in flight at once
+  float2 ml = {-INFINITY, 0.0f};
+  if (lane < nsp) ml = *reinterpret_cast<const float2*>(pmlw);
   float4 v[kBatch];
   auto load_batch = [&](int k0) {
-    const char* pk = reinterpret_cast<const char*>(ob + (size_t)k0 * bstride);   // uniform
+    const char* pk = reinterpret_cast<const char*>(ob + (size_t)k0 * SG * R * D);   // uniform
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       if (k0 + k >= nb) break;
-      v[k] = *reinterpret_cast<const float4*>(pk + (k0 + k < nfull ? boff : boffx));
-      pk += (size_t)bstride * 4;
+      v[k] = *reinterpret_cast<const float4*>(pk + (k0 + k < nb - 1 ? boff : boffx));
+      pk += (size_t)SG * R * D * 4;
     }
   };
-  if (active) load_batch(0);
-  // weights exp2(m_s - M) / sum_s exp2(m_s - M) l_s
-#pragma unroll
-  for (int k = 0; k < kRowsPerWave; ++k) {
-    const int rr = wave + kWaves * k;
-    if (rr >= R) break;
-    const float M = wave_max(ml[k].x);
-    const float e = lane < nsp ? __builtin_amdgcn_exp2f(ml[k].x - M) : 0.0f;
-    const float den = wave_sum(e * ml[k].y);
-    if (lane < nsp) sw[lane * R + rr] = e / den;
-  }
-  __syncthreads();
-
+  load_batch(0);
+  // weights exp2(m_s - M) / sum_s exp2(m_s - M) l_s, in lane s (0 past nsp)
+  const float M = wave_max(ml.x);
+  const float e = lane < nsp ? __builtin_amdgcn_exp2f(ml.x - M) : 0.0f;
+  const float w = e / wave_sum(e * ml.y);
   float4 a = {0.0f, 0.0f, 0.0f, 0.0f};
   auto add_batch = [&](int k0) {
-    float w[kBatch];
-    const float* swk = sw + k0 * tpc * R;                 // uniform
+    float wk[kBatch];
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       if (k0 + k >= nb) break;
-      const bool full = k0 + k < nfull;
-      const float x = swk[full ? wo : wox];
-      w[k] = full || extra ? x : 0.0f;
-      swk += tpc * R;
+      wk[k] = __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute((g + SG * (k0 + k)) << 2,
+                                                                     __builtin_bit_cast(int, w)));
     }
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
       if (k0 + k >= nb) break;
-      a.x = fmaf(w[k], v[k].x, a.x);
-      a.y = fmaf(w[k], v[k].y, a.y);
-      a.z = fmaf(w[k], v[k].z, a.z);
-      a.w = fmaf(w[k], v[k].w, a.w);
+      a.x = fmaf(wk[k], v[k].x, a.x);
+      a.y = fmaf(wk[k], v[k].y, a.y);
+      a.z = fmaf(wk[k], v[k].z, a.z);
+      a.w = fmaf(wk[k], v[k].w, a.w);
     }
   };
-  if (active) {
-    add_batch(0);
-    // more splits than one batch covers (large row groups): further batches
-    for (int k0 = kBatch; k0 < nb; k0 += kBatch) {
-      load_batch(k0);
-      add_batch(k0);
-    }
+  add_batch(0);
+  // more splits than one batch covers: further batches
+  for (int k0 = kBatch; k0 < nb; k0 += kBatch) {
+    load_batch(k0);
+    add_batch(k0);
   }
-  if (active) red[part * cols + c] = a;
-  __syncthreads();
-  for (int cc = tid; cc < cols; cc += kThreads) {
-    float4 o = red[cc];
-    for (int pp = 1; pp < tpc; ++pp) {
-      const float4 b = red[pp * cols + cc];
-      o.x += b.x;
-      o.y += b.y;
-      o.z += b.z;
-      o.w += b.w;
-    }
-    *reinterpret_cast<float4*>(cc == tid ? dst : out_row((4 * cc) / D) + (4 * cc - ((4 * cc) / D) * D)) = o;
-  }
+  // the split groups: lanes c + CR * g, summed in a fixed order
+  auto fold = [&](auto swap) {
+    a.x = swap(a.x);
+    a.y = swap(a.y);
+    a.z = swap(a.z);
+    a.w = swap(a.w);
+  };
+  if constexpr (SG == 4) fold([](float x) { return across16(x, fadd); });
+  fold([](float x) { return across32(x, fadd); });
+  if (g == 0) *reinterpret_cast<float4*>(dst) = a;
   if (tid == 0) {
     if (ts) ts[kStDone] = now_stamp();
     __hip_atomic_store(&p.counters[((size_t)seq * p.n_kv_heads + kvh) * kCounterStride], 0u, __ATOMIC_RELAXED,
