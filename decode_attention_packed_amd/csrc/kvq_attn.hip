@@ -989,14 +989,17 @@ __device__ __forceinline__ void finish_split(const AttnParams& p, uint8_t* s_lds
   // partial outputs, all in flight at once
   float2 ml = {-INFINITY, 0.0f};
   if (lane < nsp) ml = *reinterpret_cast<const float2*>(pmlw);
+  // Every batch issues all kBatch loads (those past the last batch repeat
+  // its addresses, with weight 0 below): with a fixed count and no branch
+  // between them, the weights wait for the maxima alone, not for the rows.
   float4 v[kBatch];
   auto load_batch = [&](int k0) {
-    const char* pk = reinterpret_cast<const char*>(ob + (size_t)k0 * SG * R * D);   // uniform
+    const char* pk = reinterpret_cast<const char*>(ob + (size_t)min(k0, nb - 1) * SG * R * D);   // uniform
 #pragma unroll
     for (int k = 0; k < kBatch; ++k) {
-      if (k0 + k >= nb) break;
-      v[k] = *reinterpret_cast<const float4*>(pk + (k0 + k < nb - 1 ? boff : boffx));
-      pk += (size_t)SG * R * D * 4;
+      const bool inner = k0 + k < nb - 1;
+      v[k] = *reinterpret_cast<const float4*>(pk + (inner ? boff : boffx));
+      if (inner) pk += (size_t)SG * R * D * 4;
     }
   };
   load_batch(0);
