@@ -1692,20 +1692,32 @@ __device__ __forceinline__ void split_merge_body(const AttnParams& p, int blk) {
   // Every slot of the group's partials (n_split of them) lies inside the
   // workspace, so the maxima, sums and the first kPre partial rows are all
   // loaded before the length says how many splits ran: one memory round
-  // trip.  Slots past that count hold stale values and are never used.
+  // trip.  Slots past that count hold stale values and are never used.  All
+  // kPre loads are issued (slots past n_split repeat the last one): with a
+  // fixed count and no branch between them the compiler keeps them ahead of
+  // the weights, which then wait for the maxima alone (loads under a
+  // per-slot condition were moved below the weights, a second round trip).
   const size_t pbase = (size_t)grp * p.n_split;
   const int nmax = min(p.n_split, kPre);
-  float2 ml = {-INFINITY, 0.0f};
-  if (lane < p.n_split) ml = *reinterpret_cast<const float2*>(p.part_ml + ((pbase + lane) * R + r) * 2);
-  const float* ob = p.part_o + (pbase * R + r) * D + C * lane;
+  // (lanes past n_split load slot 0's pair; the weights below mask them)
+  const float2 ml = *reinterpret_cast<const float2*>(
+      p.part_ml + ((pbase + (lane < p.n_split ? lane : 0)) * R + r) * 2);
+  // row r of split 0 (uniform) and this lane's byte offset in a row
+  const char* const ob = reinterpret_cast<const char*>(p.part_o + (pbase * R + r) * D);
+  const uint32_t lo = (uint32_t)(C * lane * 4);
+  auto load_slot = [&](int k, float (&x)[C]) {
+    const char* row = ob + (size_t)k * R * D * 4;   // uniform
+    if constexpr (C == 2) {
+      const float2 t = *reinterpret_cast<const float2*>(row + lo);
+      x[0] = t.x;
+      x[1] = t.y;
+    } else {
+      x[0] = *reinterpret_cast<const float*>(row + lo);
+    }
+  };
   float v[kPre][C];
 #pragma unroll
-  for (int k = 0; k < kPre; ++k) {
-    if (k < nmax) {
-#pragma unroll
-      for (int c = 0; c < C; ++c) v[k][c] = ob[(size_t)k * R * D + c];
-    }
-  }
+  for (int k = 0; k < kPre; ++k) load_slot(min(k, nmax - 1), v[k]);
   const int L = p.seq_len[seq];
   // (seq_len above max_seq_len breaks the call's contract; the clamp keeps
   // the reads inside this group's partials even then)
@@ -1719,35 +1731,36 @@ __device__ __forceinline__ void split_merge_body(const AttnParams& p, int blk) {
   float acc[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) acc[c] = 0.0f;
+  // Every slot's sum is formed and kept only below nsp (a select, not a
+  // branch: under a branch the compiler moved each slot's load into it,
+  // after the weights, one round trip per slot).
 #pragma unroll
   for (int k = 0; k < kPre; ++k) {
-    if (k < nsp) {
-      const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
+    const float wk = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k));
 #pragma unroll
-      for (int c = 0; c < C; ++c) acc[c] = fmaf(wk, v[k][c], acc[c]);
+    for (int c = 0; c < C; ++c) {
+      const float t = fmaf(wk, v[k][c], acc[c]);
+      acc[c] = k < nsp ? t : acc[c];
     }
   }
   // more than kPre splits: the rest in batches of kPre, each batch's loads
   // all in flight before its sums
   for (int k0 = kPre; k0 < nsp; k0 += kPre) {
 #pragma unroll
-    for (int k = 0; k < kPre; ++k) {
-      if (k0 + k < nsp) {
-#pragma unroll
-        for (int c = 0; c < C; ++c) v[k][c] = ob[(size_t)(k0 + k) * R * D + c];
-      }
-    }
+    for (int k = 0; k < kPre; ++k) load_slot(min(k0 + k, nsp - 1), v[k]);
+    // (these slots all ran: the repeats of slot nsp - 1 are finite and
+    // carry weight 0)
 #pragma unroll
     for (int k = 0; k < kPre; ++k) {
-      if (k0 + k < nsp) {
-        const float wk =
-            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), k0 + k));
+      const float wk = k0 + k < nsp ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                                     __builtin_bit_cast(int, w), (k0 + k) & 63))
+                                    : 0.0f;
 #pragma unroll
-        for (int c = 0; c < C; ++c) acc[c] = fmaf(wk, v[k][c], acc[c]);
-      }
+      for (int c = 0; c < C; ++c) acc[c] = fmaf(wk, v[k][c], acc[c]);
     }
   }
-  float* dst = p.out + (((size_t)seq * p.n_qtok + r / G) * p.n_q_heads + kvh * G + r % G) * D + C * lane;
+  const int t = small_div(r, p.rcp_group);
+  float* dst = p.out + (((size_t)seq * p.n_qtok + t) * p.n_q_heads + kvh * G + r - t * G) * D + C * lane;
 #pragma unroll
   for (int c = 0; c < C; ++c) dst[c] = acc[c];
 }
