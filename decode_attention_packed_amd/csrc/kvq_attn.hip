@@ -432,23 +432,71 @@ __device__ __forceinline__ void wait_tiles(int pending) {
 // let a wave that runs ahead take more, 1-2 us faster on the verify step,
 // but then which tiles share a wave's running maximum, and with it the fp16
 // rounding of the P.V operand, changed from run to run.)
+//
+// The SIMDs issue their oldest wave first, so with an even deal the first
+// wave on each SIMD (waves 0-3) finishes well ahead of the others: by ~7 us
+// in the verify step's 128-tile chunks (row layout, 8 waves) and ~6 us in
+// the ragged batch (column layout, head_dim 64), leaving one wave per SIMD
+// for the rest of the chunk.  Those kernels therefore deal the last tiles
+// of a chunk of at least kSkewMin tiles round-robin to waves 0-3 only (a
+// fraction SF/64 of the chunk, at most a cap: kSkewF, kSkewCap), still a
+// fixed map: half of the row layout's chunk up to 32 tiles (the gap is
+// about the same in 64- and 128-tile chunks), 5/64 of the column layout's
+// at head_dim 64.  In the 12-wave
+// build of the long single-query step the three waves per SIMD finish ~5
+// and ~9 us apart as well, but a CU's remaining waves still keep enough
+// tiles in flight, and skewed deals measured slower there; chunks shorter
+// than kSkewMin (where the deal decides the end) keep the even one.
+#ifndef KVQ_SKEW_ROWS_CAP
+#define KVQ_SKEW_ROWS_CAP 32  // row layout: half the chunk, at most 32 tiles
+#endif
 constexpr int kWaveStride = kTile * kWaves;
+constexpr int kFastWaves = 4;                       // the first wave on each SIMD
+constexpr int kSkewMin = 64;                        // tiles
+constexpr int kNoTile = 0x3fffffff;                 // past every chunk
+template <bool ROWS, int D>
+constexpr int kSkewF = kWaves != 8 ? 0 : ROWS ? 32 : D == 64 ? 5 : 0;
+template <bool ROWS>
+constexpr int kSkewCap = ROWS ? KVQ_SKEW_ROWS_CAP : 1 << 20;
 
 // A wave's tiles in flight: `cur` is the next one to process, `n1` was
 // issued after it, `g` is the one after `n1`, not issued yet.  Tile starts
-// only grow, so once one is past the chunk end all later ones are.
+// only grow, so once one is past the chunk end all later ones are.  Tiles
+// from `tail` on are the skewed tail (tail is the chunk end when there is
+// none).
 struct TileQueue {
   int cur, n1, g;
+  int tail, wave;
 };
-__device__ __forceinline__ TileQueue first_tiles(int c0, int wave) {
-  const int t = c0 + kTile * wave;
-  return {t, t + kWaveStride, t + 2 * kWaveStride};
+template <int SF>
+__device__ __forceinline__ int next_tile(const TileQueue& q, int t) {
+  if constexpr (SF == 0) {
+    return t + kWaveStride;
+  } else {
+    if (t >= q.tail) return t >= kNoTile ? kNoTile : t + kTile * kFastWaves;
+    const int t2 = t + kWaveStride;
+    if (t2 < q.tail) return t2;
+    return q.wave < kFastWaves ? q.tail + kTile * q.wave : kNoTile;
+  }
+}
+template <int SF, int CAP>
+__device__ __forceinline__ TileQueue first_tiles(int c0, int wave, int chunk) {
+  TileQueue q;
+  const int ct = chunk / kTile;
+  q.tail = c0 + (SF > 0 && ct >= kSkewMin ? chunk - kTile * min((ct * SF) >> 6, CAP) : chunk);
+  q.wave = wave;
+  int t = c0 + kTile * wave;
+  if (SF > 0 && t >= q.tail) t = wave < kFastWaves ? q.tail + kTile * wave : kNoTile;
+  q.cur = t;
+  q.n1 = next_tile<SF>(q, t);
+  q.g = next_tile<SF>(q, q.n1);
+  return q;
 }
 
 // One step of a wave's ring: refill and wait as the slot count allows, then
 // run `body` on the tile in slot SLOT (a compile-time slot, so LDS offsets
 // become immediates).  Returns false once the wave's tiles are done.
-template <int D, int VF, int SLOT, class Body>
+template <int D, int VF, int SLOT, int SF, class Body>
 __device__ __forceinline__ bool ring_step(const AttnParams& p, int seq, int kvh, int c1,
                                           uint32_t ring_lds, const TileLane<D, VF>& tl,
                                           TileCursor& cur, TileQueue& q, Body& body) {
@@ -458,7 +506,7 @@ __device__ __forceinline__ bool ring_step(const AttnParams& p, int seq, int kvh,
     // the next tile goes into the slot freed last step
     const int n2 = q.g;
     if (n2 < c1) issue_tile<D, VF>(p, seq, kvh, n2, ring_lds + ((SLOT + 2) % 3) * S::BYTES, tl, cur);
-    q.g = n2 + kWaveStride;
+    q.g = next_tile<SF>(q, n2);
     wait_tiles<S::LPT>((q.n1 < c1) + (n2 < c1));
     body(std::integral_constant<int, SLOT>{}, q.cur);
     q.cur = q.n1;
@@ -469,25 +517,25 @@ __device__ __forceinline__ bool ring_step(const AttnParams& p, int seq, int kvh,
     if (q.g < c1) issue_tile<D, VF>(p, seq, kvh, q.g, ring_lds + SLOT * S::BYTES, tl, cur);
     q.cur = q.n1;
     q.n1 = q.g;
-    q.g += kWaveStride;
+    q.g = next_tile<SF>(q, q.g);
   }
   return true;
 }
 
 // Run a wave's ring to the end.  On entry tile q.cur sits in slot 0 and
 // q.n1 in slot 1 (both issued or past the end).
-template <int D, int VF, class Body>
+template <int D, int VF, int SF, class Body>
 __device__ __forceinline__ void run_ring(const AttnParams& p, int seq, int kvh, int c1,
                                          uint32_t ring_lds, const TileLane<D, VF>& tl,
                                          TileCursor& cur, TileQueue& q, Body& body) {
   if constexpr (Slot<D, VF>::NSLOT == 3) {
-    while (ring_step<D, VF, 0>(p, seq, kvh, c1, ring_lds, tl, cur, q, body) &&
-           ring_step<D, VF, 1>(p, seq, kvh, c1, ring_lds, tl, cur, q, body) &&
-           ring_step<D, VF, 2>(p, seq, kvh, c1, ring_lds, tl, cur, q, body)) {
+    while (ring_step<D, VF, 0, SF>(p, seq, kvh, c1, ring_lds, tl, cur, q, body) &&
+           ring_step<D, VF, 1, SF>(p, seq, kvh, c1, ring_lds, tl, cur, q, body) &&
+           ring_step<D, VF, 2, SF>(p, seq, kvh, c1, ring_lds, tl, cur, q, body)) {
     }
   } else {
-    while (ring_step<D, VF, 0>(p, seq, kvh, c1, ring_lds, tl, cur, q, body) &&
-           ring_step<D, VF, 1>(p, seq, kvh, c1, ring_lds, tl, cur, q, body)) {
+    while (ring_step<D, VF, 0, SF>(p, seq, kvh, c1, ring_lds, tl, cur, q, body) &&
+           ring_step<D, VF, 1, SF>(p, seq, kvh, c1, ring_lds, tl, cur, q, body)) {
     }
   }
 }
@@ -768,7 +816,7 @@ struct WgStart {
   bool off_xcd;
   AppendRange app;
 };
-template <int D, int VF>
+template <int D, int VF, int SF, int CAP>
 __device__ __forceinline__ bool wg_start(const AttnParams& p, int blk, uint8_t* s_lds, int wave,
                                          uint8_t* s_patch, const TileLane<D, VF>& tl,
                                          TileCursor& cur, TileQueue& tq, int8_t*& s_qc,
@@ -783,7 +831,7 @@ __device__ __forceinline__ bool wg_start(const AttnParams& p, int blk, uint8_t* 
   const bool guess = bc.len < 0 && p.seg_table == nullptr;
   const int Ls = bc.len >= 0 ? bc.len : (guess ? p.max_len : load_uniform(p.seq_len + w.seq));
   if (w.c0 >= Ls) return false;   // no tokens here even at the bound
-  tq = first_tiles(w.c0, wave);
+  tq = first_tiles<SF, CAP>(w.c0, wave, p.chunk);
   const int cs1 = min(w.c0 + p.chunk, Ls);
   const AppendRange app_s = append_range(p, Ls, w.c0, cs1);
   const int n_issued = prologue_issue<D, VF>(p, s_lds, w.seq, w.kvh, wave, Ls, cs1, app_s, tl, cur, tq);
@@ -1258,7 +1306,8 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   float* s_qd;
   uint8_t* s_patch = s_lds + RING;
   WgStart ws;
-  if (!wg_start<D, VF>(p, blk, s_lds, wave, s_patch, tl, cur, tq, s_qc, s_qd, ws)) return;
+  constexpr int SF = kSkewF<true, D>;
+  if (!wg_start<D, VF, SF, kSkewCap<true>>(p, blk, s_lds, wave, s_patch, tl, cur, tq, s_qc, s_qd, ws)) return;
   const int split = ws.split, kvh = ws.kvh, seq = ws.seq, L = ws.L, n_split_seq = ws.n_split_seq;
   const int c1 = ws.c1;
   const AppendRange app = ws.app;
@@ -1316,7 +1365,7 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
     if (t0 + kTile > app.lo && t0 < app.hi) patch_tile<D, VF>(ring + SL * S::BYTES, s_patch, t0, app);
     process_tile<D, VF, DBG>(ring + SL * S::BYTES, pbuf, t0, c1, qa, dqs, vis, st, dbg);
   };
-  run_ring<D, VF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
+  run_ring<D, VF, SF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
   // a tile issued before the length was known and past it may still land
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if constexpr (DBG == 2) {
@@ -1561,7 +1610,8 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
   float* s_qd;
   uint8_t* s_patch = s_lds + RING;
   WgStart ws;
-  if (!wg_start<D, VF>(p, blk, s_lds, wave, s_patch, tl, cur, tq, s_qc, s_qd, ws)) return;
+  constexpr int SF = kSkewF<false, D>;
+  if (!wg_start<D, VF, SF, kSkewCap<false>>(p, blk, s_lds, wave, s_patch, tl, cur, tq, s_qc, s_qd, ws)) return;
   const int split = ws.split, kvh = ws.kvh, seq = ws.seq, L = ws.L, n_split_seq = ws.n_split_seq;
   const int c1 = ws.c1;
   const AppendRange app = ws.app;
@@ -1625,7 +1675,7 @@ __device__ __forceinline__ void attn_cols_body(const AttnParams& p, int blk) {
                                   valid, qb, wq, st, dbg);
     first = false;
   };
-  run_ring<D, VF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
+  run_ring<D, VF, SF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
   // a tile issued before the length was known and past it may still land
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   if constexpr (DBG == 2) {
