@@ -36,8 +36,10 @@
 //          S.V), so one 8-byte read is 8 tokens of one dim.
 //
 // Row layout (larger groups, e.g. 4 query tokens x 4 heads): the 16 MFMA
-// rows are query rows; the per-block dots come from one MFMA per block, P
-// goes through LDS into the A operand and B is the dequantized V.
+// columns are query rows; the per-block dots come from one MFMA per block
+// (S^T = K Q^T, the tile's tokens dealt to the MFMA rows so that each lane
+// receives its row's weights in the order the P.V operand takes them), and
+// P.V runs transposed as in the column layout, P straight from registers.
 //
 // The waves merge through LDS and the work-group writes one unnormalized
 // partial (m, l, o) per row.  Column layout: the last work-group to finish a
@@ -250,9 +252,6 @@ struct Slot {
   static constexpr int DV_OFF = DK_OFF + (kF16K ? 0 : SBYTES);
   static constexpr int BYTES = DV_OFF + SBYTES;
   static constexpr int CPR = KROW / 16;              // 16-byte chunks per K row
-  static constexpr int PBYTES = kRows * (kTile + 4) * 4;   // padded P staging tile (row layout)
-  static constexpr bool P_IN_K = PBYTES <= KBYTES;   // P can reuse the K area
-  static constexpr int PBUF = P_IN_K ? 0 : kWaves * PBYTES;   // row layout only
   // packed bytes of one appended token in the patch buffer: K row, K scales,
   // V row, V scales
   static constexpr int PK = 0, PKS = D, PV = D + 2 * NB, PVS = D + 2 * NB + VROW;
@@ -260,7 +259,7 @@ struct Slot {
   static constexpr int PATCH = kMaxAppend * PTOK;   // patch buffer, after the ring
   // three slots per wave where they fit in the CU's LDS, else two; head_dim
   // 64 takes two so that two work-groups share a CU (see kOccupancy)
-  static constexpr int NSLOT = (D != 64 && 3 * BYTES * kWaves + PBUF + PATCH <= kLdsBudget) ? 3 : 2;
+  static constexpr int NSLOT = (D != 64 && 3 * BYTES * kWaves + PATCH <= kLdsBudget) ? 3 : 2;
   static constexpr int RPW = (kRows + kWaves - 1) / kWaves;   // Q rows per wave
   static constexpr int QSTAGE = RPW * D * 4;         // fp32 Q rows of one wave
   // Q operands shared through wave 0's last slot: int8 codes and fp32 block
@@ -275,7 +274,7 @@ struct Slot {
   static_assert(KBYTES % 1024 == 0 && VBYTES % 1024 == 0, "whole 1 KB load steps");
   static_assert(!kF16K || SBYTES == 256, "fp16 K: the V scale plane is one 256-byte load");
   static_assert(QSTAGE + QOPS <= BYTES, "Q staging does not fit a slot");
-  static_assert(NSLOT * BYTES * kWaves + PBUF + PATCH <= kLdsBudget, "ring does not fit the LDS");
+  static_assert(NSLOT * BYTES * kWaves + PATCH <= kLdsBudget, "ring does not fit the LDS");
   static_assert(STAGE + STAGE_UNITS * D * 4 <= BYTES, "appended rows do not fit a slot");
 };
 
@@ -1108,36 +1107,40 @@ __device__ __forceinline__ float mul_f32_f16(float wq, uint32_t pair) {
   return __builtin_fmaf(wq, (float)(HI ? d.y : d.x), 0.0f);
 }
 
-// Running state of one wave: output tiles (rows 4*(lane/16)+i, dims
-// 16n + lane%16) and the per-row running maximum and sum of weights.
+// Running state of one wave: output tiles acc[n][i] = row l%16, dim
+// 16n + 4(l/16) + i; the running maximum of row l%16 and the sum of the
+// weights of this lane's tokens (the four lanes of a row are summed once, at
+// the end of the ring).
 template <int D>
 struct WaveState {
   v4f acc[D / 16];
-  float mrow[4];
-  float lrow[4];
+  float mrow;
+  float lrow;
 };
 
 // One 32-token tile from its LDS slot: scores, online softmax update, P.V.
-// P is staged in the slot's K area when it fits, else in `pbuf`.
+// Both products run transposed, S^T = K Q^T and O^T += V^T P^T.  Score MFMA
+// h takes token 8(m/4) + 4h + m%4 as its row m, so lane l receives the
+// scores of row l%16 for tokens 8(l/16) + 4h + i: over h and i, the 8 tokens
+// 8(l/16) .. +8, which is the k-range of lane l's B operand in the P.V MFMA.
+// P thus stays in registers, and the row maximum is an in-lane max plus two
+// exchanges between the lanes of a row.  `full`: every token of the tile is
+// visible to every query row (no mask).
 template <int D, int VF, int DBG = 0>
-__device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0, int c1,
-                                             const long (&qa)[D / kBlock],
-                                             const float (&dqs)[4][D / kBlock], const int (&vis)[4],
-                                             WaveState<D>& st, int32_t* const (&dbg)[4] = {}) {
+__device__ __forceinline__ void process_tile(uint8_t* slot, int t0, int c1, bool full,
+                                             const long (&qa)[D / kBlock], const float (&dq)[D / kBlock],
+                                             int vis, WaveState<D>& st, int32_t* dbg) {
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
-  constexpr int PSTRIDE = kTile + 4;   // padded row of the P staging tile (floats)
   const int lane = __lane_id();
   const int col = lane & 15, grp = lane >> 4;
   v4f(&acc)[D / 16] = st.acc;
-  float(&mrow)[4] = st.mrow;
-  float(&lrow)[4] = st.lrow;
 
-  // ---- scores (log2 domain) of rows 4*grp+i, tokens t0 + 16*h + col
+  // ---- scores (log2 domain) of row col, tokens t0 + 8*grp + 4h + i
   float s[2][4];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int r = 16 * h + col;
+    const int r = 8 * (col >> 2) + 4 * h + (col & 3);   // this lane's K row in MFMA h
     long kb[NB];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -1145,75 +1148,59 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
       kb[b] = *reinterpret_cast<const long*>(slot + S::K_OFF + (r * S::CPR + (q ^ kswz<S::CPR>(r))) * 16 +
                                              8 * (grp & 1));
     }
-    _Float16 dk[NB];   // scale b of token r sits at slot b*32 + r
+    // K scales of the 4 output tokens (scale b of token t sits at b*32 + t)
+    uint2 dk[NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) dk[b] = reinterpret_cast<const _Float16*>(slot + S::DK_OFF)[b * kTile + r];
+    for (int b = 0; b < NB; ++b)
+      dk[b] = *reinterpret_cast<const uint2*>(slot + S::DK_OFF + (b * kTile + 8 * grp + 4 * h) * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[h][i] = 0.0f;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      const v4i c = qk_block_mfma(qa[b], kb[b]);
+      const v4i c = qk_block_mfma(kb[b], qa[b]);
       if constexpr (DBG == 1) {
-        // the test hook: row 4*grp + i, token t0 + r, block b
-        if (t0 + r < c1)
+        // the test hook: row col, token t0 + 8*grp + 4h + i, block b
+        if (dbg)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            if (dbg[i]) dbg[i][(size_t)(t0 + r) * NB + b] = c[i];
+          for (int i = 0; i < 4; ++i) {
+            const int t = t0 + 8 * grp + 4 * h + i;
+            if (t < c1) dbg[(size_t)t * NB + b] = c[i];
+          }
       }
-      const float dkf = (float)dk[b];
+      const float w[4] = {mul_f32_f16<0>(dq[b], dk[b].x), mul_f32_f16<1>(dq[b], dk[b].x),
+                          mul_f32_f16<0>(dq[b], dk[b].y), mul_f32_f16<1>(dq[b], dk[b].y)};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[h][i] = fmaf((float)c[i], dqs[i][b] * dkf, s[h][i]);
+      for (int i = 0; i < 4; ++i) s[h][i] = fmaf((float)c[i], w[i], s[h][i]);
     }
-    const int t = t0 + r;
+    if (!full) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[h][i] = t < vis[i] ? s[h][i] : -INFINITY;
+      for (int i = 0; i < 4; ++i) s[h][i] = t0 + 8 * grp + 4 * h + i < vis ? s[h][i] : -INFINITY;
+    }
   }
 
-  // ---- online softmax: row maxima over the tile, rescale when they grow
-  float mnew[4];
-  bool grow = false;
+  // ---- online softmax: the row maximum over the tile, rescale when it grows
+  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  mx = across32(across16(mx, fmax2), fmax2);
+  const float mnew = fmaxf(st.mrow, mx);
+  if (__any(mnew > st.mrow)) {
+    const float a = __builtin_amdgcn_exp2f(st.mrow - mnew);
+    st.lrow *= a;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    mnew[i] = fmaxf(mrow[i], max_row16(fmaxf(s[0][i], s[1][i])));
-    grow |= mnew[i] > mrow[i];
+    for (int n = 0; n < D / 16; ++n) acc[n] *= a;
+    st.mrow = mnew;
   }
-  if (__any(grow)) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = __builtin_amdgcn_exp2f(mrow[i] - mnew[i]);
-      lrow[i] *= a;
-#pragma unroll
-      for (int n = 0; n < D / 16; ++n) acc[n][i] *= a;
-      mrow[i] = mnew[i];
-    }
-  }
-  // P goes through the slot's K area (every K read of this tile is done)
-  float* sP = S::P_IN_K ? reinterpret_cast<float*>(slot + S::K_OFF) : pbuf;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  float mshift[4];   // the running maxima less the P.V shift
-#pragma unroll
-  for (int i = 0; i < 4; ++i) mshift[i] = mrow[i] - kPvShift<VF>;
+  const float mshift = st.mrow - kPvShift<VF>;   // the running maximum less the P.V shift
+  float pr[8];   // weights of row col, tokens t0 + 8*grp + j
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float e = __builtin_amdgcn_exp2f(s[h][i] - mshift[i]);
-      lrow[i] += e;
-      sP[(4 * grp + i) * PSTRIDE + 16 * h + col] = e;
+      pr[4 * h + i] = __builtin_amdgcn_exp2f(s[h][i] - mshift);
+      st.lrow += pr[4 * h + i];
     }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // ---- A operands: row col, tokens 8*grp .. +8, times the V block scale
-  float pr[8];
-  {
-    const float4 a0 = *reinterpret_cast<const float4*>(sP + col * PSTRIDE + 8 * grp);
-    const float4 a1 = *reinterpret_cast<const float4*>(sP + col * PSTRIDE + 8 * grp + 4);
-    pr[0] = a0.x; pr[1] = a0.y; pr[2] = a0.z; pr[3] = a0.w;
-    pr[4] = a1.x; pr[5] = a1.y; pr[6] = a1.z; pr[7] = a1.w;
-  }
+  // ---- B operands: row col, tokens 8*grp .. +8, times the V block scale
   v8h dv[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b)
@@ -1234,18 +1221,18 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
     uint32_t hw[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) hw[k] = round_f16_pair(pr[2 * k], pr[2 * k + 1], dvw[k]);
-    const v8h ahi = __builtin_bit_cast(v8h, hw);
+    const v8h pb = __builtin_bit_cast(v8h, hw);
     if constexpr (VF == 0) {
-      // byte = nibble(dim 32b + col) | nibble(dim 32b + 16 + col) << 4, 8
+      // A: byte = nibble(dim 32b + col) | nibble(dim 32b + 16 + col) << 4, 8
       // tokens; the high nibble is used in place, as 16 * (n - 8) (exact), and
       // the factor 16 is taken out of those accumulators at the end
       const int R = 16 * b + col;
       const uint2 w = *reinterpret_cast<const uint2*>(
           slot + S::V_OFF + (R * 2 + ((grp >> 1) ^ ((R >> 2) & 1))) * 16 + 8 * (grp & 1));
-      const v8h blo = bytes_to_f16x8(w.x & 0x0F0F0F0Fu, w.y & 0x0F0F0F0Fu, (_Float16)1032.0f);
-      const v8h bhi = bytes_to_f16x8(w.x & 0xF0F0F0F0u, w.y & 0xF0F0F0F0u, (_Float16)1152.0f);
-      acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, blo, acc[2 * b], 0, 0, 0);
-      acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bhi, acc[2 * b + 1], 0, 0, 0);
+      const v8h alo = bytes_to_f16x8(w.x & 0x0F0F0F0Fu, w.y & 0x0F0F0F0Fu, (_Float16)1032.0f);
+      const v8h ahi = bytes_to_f16x8(w.x & 0xF0F0F0F0u, w.y & 0xF0F0F0F0u, (_Float16)1152.0f);
+      acc[2 * b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, pb, acc[2 * b], 0, 0, 0);
+      acc[2 * b + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, pb, acc[2 * b + 1], 0, 0, 0);
     } else {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -1254,8 +1241,8 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, float* pbuf, int t0,
         const uint2 w = *reinterpret_cast<const uint2*>(
             slot + S::V_OFF + (R * 2 + ((grp >> 1) ^ ((R >> 2) & 1))) * 16 + 8 * (grp & 1));
         // int8 code c -> byte c ^ 0x80 = c + 128 -> fp16 (1024 + c + 128) - 1152
-        const v8h bv = bytes_to_f16x8(w.x ^ 0x80808080u, w.y ^ 0x80808080u, (_Float16)1152.0f);
-        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bv, acc[n], 0, 0, 0);
+        const v8h av = bytes_to_f16x8(w.x ^ 0x80808080u, w.y ^ 0x80808080u, (_Float16)1152.0f);
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pb, acc[n], 0, 0, 0);
       }
     }
   }
@@ -1283,7 +1270,7 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   using S = Slot<D, VF>;
   constexpr int NB = D / kBlock;
   constexpr int NT = D / 16;
-  constexpr int RING = kWaves * S::NSLOT * S::BYTES + S::PBUF;
+  constexpr int RING = kWaves * S::NSLOT * S::BYTES;
   constexpr int LDS_BYTES = RING + S::PATCH;
   constexpr int WAVE_BYTES = S::NSLOT * S::BYTES;   // one wave's ring slots, later its merge block
   constexpr int DP = D + 4;                         // merge rows: a lane's 4 rows on distinct banks
@@ -1322,18 +1309,16 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
     }
   }
   bool first_tile = true;
+  // Q operands and block scales of row col (zero codes and scales on padding
+  // rows), and the tokens it sees: tokens below `vis`; below `vis_lo` every
+  // row sees them
   long qa[NB];
   load_q_operands<D>(s_qc, qa);
-  float dqs[4][NB];
-  int vis[4];
+  float dq[NB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 4 * grp + i;
-#pragma unroll
-    for (int b = 0; b < NB; ++b) dqs[i][b] = s_qd[r * NB + b] * p.scale_log2;
-    const int v = p.causal ? L - p.n_qtok + r / G + 1 : L;
-    vis[i] = min(r < R ? v : 0, c1);
-  }
+  for (int b = 0; b < NB; ++b) dq[b] = s_qd[col * NB + b] * p.scale_log2;
+  const int vis = min(col < R ? (p.causal ? L - p.n_qtok + col / G + 1 : L) : 0, c1);
+  const int vis_lo = min(p.causal ? L - p.n_qtok + 1 : L, c1);
   __syncthreads();   // every wave has its operands; wave 0's last slot is free
   // the packed appended rows go out now, ahead of this wave's next tile, so
   // their stores are acknowledged long before the partial is published
@@ -1343,18 +1328,12 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   WaveState<D> st;
 #pragma unroll
   for (int n = 0; n < NT; ++n) st.acc[n] = (v4f){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    st.mrow[i] = -1e30f;
-    st.lrow[i] = 0.0f;
-  }
+  st.mrow = -1e30f;
+  st.lrow = 0.0f;
   uint8_t* ring = s_lds + wave * S::NSLOT * S::BYTES;
-  float* pbuf = reinterpret_cast<float*>(s_lds + kWaves * S::NSLOT * S::BYTES + wave * S::PBYTES);
-  int32_t* dbg[4] = {};
+  int32_t* dbg = nullptr;
   if constexpr (DBG == 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * grp + i < R) dbg[i] = dbg_row(p, seq, kvh, 4 * grp + i, NB);
+    if (col < R) dbg = dbg_row(p, seq, kvh, col, NB);
   }
   auto body = [&](auto slot_c, int t0) {
     constexpr int SL = decltype(slot_c)::value;
@@ -1363,7 +1342,7 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
       first_tile = false;
     }
     if (t0 + kTile > app.lo && t0 < app.hi) patch_tile<D, VF>(ring + SL * S::BYTES, s_patch, t0, app);
-    process_tile<D, VF, DBG>(ring + SL * S::BYTES, pbuf, t0, c1, qa, dqs, vis, st, dbg);
+    process_tile<D, VF, DBG>(ring + SL * S::BYTES, t0, c1, t0 + kTile <= vis_lo, qa, dq, vis, st, dbg);
   };
   run_ring<D, VF, SF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
   // a tile issued before the length was known and past it may still land
@@ -1373,23 +1352,18 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
   }
 
   // ---- this wave's rows into its merge block (its own ring slots)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) st.lrow[i] = sum_row16(st.lrow[i]);
+  st.lrow = across32(across16(st.lrow, fadd), fadd);   // the four lanes of row col
   {
     float* mb = MergeBlock<D, DP>::at(s_lds, wave, WAVE_BYTES);
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       // q4_0: the high-nibble dims (odd n) accumulated 16 x their value
       const float sc = (VF == 0 && (n & 1)) ? 0.0625f : 1.0f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mb[(4 * grp + i) * DP + 16 * n + col] = st.acc[n][i] * sc;
+      *reinterpret_cast<v4f*>(mb + col * DP + 16 * n + 4 * grp) = st.acc[n] * sc;
     }
-    if (col == 0) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        mb[kRows * DP + 4 * grp + i] = st.mrow[i];
-        mb[kRows * DP + kRows + 4 * grp + i] = st.lrow[i];
-      }
+    if (grp == 0) {
+      mb[kRows * DP + col] = st.mrow;
+      mb[kRows * DP + kRows + col] = st.lrow;
     }
   }
   __syncthreads();   // every wave's merge block is written
