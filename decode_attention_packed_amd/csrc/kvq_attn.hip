@@ -1930,10 +1930,9 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
                 const float* k_new, const float* v_new, int n_new, hipStream_t stream,
                 int32_t* dbg_isum, int dbg_max_len, unsigned long long* dbg_stamps) {
 #if KVQ_KFMT == 0 && !KVQ_COLS_Q4_128
-  // the column layout with q4_0 V at head_dim 128 runs the 12-wave build
-  // when its chunks give every wave at least 4 tiles
-  if (c.head_dim == 128 && c.v_format == 0 && n_qtok * (n_q_heads / c.n_kv_heads) * (128 / kBlock) <= 16 &&
-      plan.chunk >= kW12MinChunk)
+  // q4_0 V at head_dim 128 runs the 12-wave build when its chunks give
+  // every wave at least 4 tiles
+  if (c.head_dim == 128 && c.v_format == 0 && plan.chunk >= kW12MinChunk)
     return w12::launch_attn(c, q, out, n_seq, n_qtok, n_q_heads, seg_table, max_segs, seq_len,
                             max_seq_len, plan, sm_scale, causal, workspace, k_new, v_new, n_new,
                             stream, dbg_isum, dbg_max_len, dbg_stamps);
@@ -1963,7 +1962,7 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-#if KVQ_KFMT == 0 && !KVQ_COLS_Q4_128
+#if KVQ_KFMT == 0
 template <int D, int VF>
 static void launch_batch_kernels(AttnBatch& b, bool rows, hipStream_t stream) {
   // the column layout merges in the last work-group of each group, the row
@@ -2000,6 +1999,15 @@ int launch_attn_batch(const AttnCall* calls, const SplitPlan* plans, int n_calls
   }
   const kvq_cache& c = *calls[0].cache;
   const bool rows = b.p[0].rows * (c.head_dim / kBlock) > 16;
+#if KVQ_COLS_Q4_128
+  if (c.head_dim != 128 || c.v_format != 0) return -4;   // not reached: only those calls come here
+  launch_batch_kernels<128, 0>(b, rows, stream);
+#else
+  // q4_0 V at head_dim 128 in the row layout runs the 12-wave build when
+  // every call's chunks give every wave at least 4 tiles
+  bool w12_rows = rows && c.head_dim == 128 && c.v_format == 0;
+  for (int i = 0; i < n_calls; ++i) w12_rows = w12_rows && plans[i].chunk >= kW12MinChunk;
+  if (w12_rows) return w12::launch_attn_batch(calls, plans, n_calls, workspace, stream);
   if (c.head_dim == 128) {
     if (c.v_format == 0)
       launch_batch_kernels<128, 0>(b, rows, stream);
@@ -2011,6 +2019,7 @@ int launch_attn_batch(const AttnCall* calls, const SplitPlan* plans, int n_calls
     else
       launch_batch_kernels<64, 1>(b, rows, stream);
   }
+#endif
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 #endif

@@ -77,9 +77,12 @@ struct AttnCall {
 int launch_attn_batch(const AttnCall* calls, const SplitPlan* plans, int n_calls, void* workspace,
                       hipStream_t stream);
 
-// The column-layout kernel for q4_0 V at head_dim 128 built with 12 waves per
-// work-group (kvq_attn_w12.hip); launch_attn above hands those calls to it.
+// The kernels for q4_0 V at head_dim 128 built with 12 waves per work-group
+// (kvq_attn_w12.hip); launch_attn and launch_attn_batch above hand the calls
+// with long enough chunks to them.
 namespace w12 {
+int launch_attn_batch(const AttnCall* calls, const SplitPlan* plans, int n_calls, void* workspace,
+                      hipStream_t stream);
 int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n_qtok, int n_q_heads,
                 const int32_t* seg_table, int max_segs, const int32_t* seq_len, int max_seq_len,
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,

@@ -1,0 +1,88 @@
+"""GPU parity of the row layout in the 12-wave build: q4_0 V at head_dim 128
+with more than 16 query-row x block columns (e.g. 4 causal query tokens x 4
+heads, the speculative-verify shape) runs the 12-wave kernels once its
+chunks reach 1536 tokens (12 waves x 4 tiles), in a single call and in a
+batched launch.  Every case is checked against the oracle on all query
+heads; the per-block int32 sums of the 12-wave row kernel are compared bit
+for bit.  Chunk sizes are forced through KVQ_CHUNK_TOKENS, so the lengths
+below end in short last splits and partial tiles."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+from decode_attention_packed_amd import workloads as W  # noqa: E402
+from oracle import kvq_oracle as O  # noqa: E402
+from tests import gpu_helpers as H  # noqa: E402
+from tests.test_gpu_append_fused import check_appended_rows, run_fused  # noqa: E402
+from tests.test_gpu_batch import run_batch  # noqa: E402
+from tests.test_gpu_headline import _isum_and_out, _table  # noqa: E402
+
+
+def _say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+
+
+def _inputs(L, tq, g, hkv, seed):
+    rng = np.random.default_rng(seed)
+    spec = W.CacheSpec("w12rows", 1, tq, g * hkv, hkv, 128, L, W.V_Q4_0, causal=True)
+    q = rng.standard_normal((1, tq, g * hkv, 128)).astype(np.float32)
+    k = (rng.standard_normal((1, L, hkv, 128)) * 1.5).astype(np.float32)
+    v = rng.standard_normal((1, L, hkv, 128)).astype(np.float32)
+    return W.CacheInputs(spec, q, k, v, np.array([L], np.int32), None, 1, -(-L // 64) * 64)
+
+
+# (L, chunk, query tokens, heads per kv head): 16 rows; 12 rows (4 padding
+# rows in the MFMA columns); 16 query tokens of one head each
+CASES = [(6001, 1536, 4, 4), (8191, 2048, 4, 4), (5000, 1536, 3, 4), (7001, 1536, 16, 1)]
+
+
+@pytest.mark.parametrize("L,chunk,tq,g", CASES)
+def test_w12_rows_forced_chunks(L, chunk, tq, g, monkeypatch):
+    monkeypatch.setenv("KVQ_CHUNK_TOKENS", str(chunk))
+    ci = _inputs(L, tq, g, 2, seed=L + 31 * tq + g)
+    _say(f"w12 rows L={L} chunk={chunk} tq={tq} g={g}")
+    cache, table, max_segs = H.build_cache(ci)
+    want = H.oracle_attention(ci)
+    H.assert_close(H.run_attention(cache, ci, table, max_segs), want, f"w12 rows L{L} c{chunk}")
+    del cache
+    # the fused append of the query tokens' own rows (causal verify step)
+    got, cache = run_fused(ci, tq)
+    check_appended_rows(cache, ci, tq)
+    H.assert_close(got, want, f"w12 rows fused L{L} c{chunk}")
+
+
+def test_w12_rows_block_sums_bitexact(monkeypatch):
+    """The block sums the 12-wave row kernel forms (test hook, same kernel
+    build and plan) against O.block_isum, bit for bit, and the hook's output
+    bit-identical to the plain call's."""
+    monkeypatch.setenv("KVQ_CHUNK_TOKENS", "1536")
+    ci = _inputs(4700, 4, 4, 2, seed=4700)
+    spec = ci.spec
+    _say("w12 rows block sums")
+    cache, table, max_segs = H.build_cache(ci)
+    isum, out, ref = _isum_and_out(ci, cache, _table(ci, max_segs))
+    assert np.array_equal(out.view(np.uint32), ref.view(np.uint32))
+    qc, _ = O.quantize_q(ci.q)
+    kc, _ = O.quantize_k(H.seq_rows(ci, 0, "k"))
+    G = spec.n_q_heads // spec.n_kv_heads
+    for j in range(spec.n_qtok):
+        for h in range(spec.n_q_heads):
+            want = O.block_isum(qc[0, j, h][None, :], kc[:, h // G])
+            assert np.array_equal(isum[0, j, h, :spec.ctx], want), (j, h)
+
+
+def test_w12_rows_batched_verify():
+    """Both caches of the verify recipe at 40000 tokens in one launch: the
+    joint plan's 1920-token chunks run the 12-wave batch kernels; all heads
+    of both calls against the oracle."""
+    cis = W.make_inputs("verify128k", ctx=40000)
+    _say("w12 rows batched verify 40000")
+    outs, _ = run_batch(cis)
+    for ci, got in zip(cis, outs):
+        H.assert_close(got, H.oracle_attention(ci), "w12 batched verify " + ci.spec.name)
