@@ -255,7 +255,7 @@ def _profile_info() -> dict:
                            bytes=8192 * 8 * per(wl["gqa8k"].caches[1]), tiles=256 * 8),
         "verify128k": dict(what="verify step (main and draft caches at 131072 tokens, one batched launch "
                                 "and its split-merge launch)",
-                           kernels=("kvq::k_attn_rows_batch<128, 0>", "kvq::k_split_merge_batch<128>"),
+                           kernels=("kvq::w12::k_attn_rows_batch<128, 0>", "kvq::w12::k_split_merge_batch<128>"),
                            bytes=131072 * (8 + 4) * per(wl["verify128k"].caches[0]), tiles=4096 * 12),
         "ragged": dict(what="ragged batch call (16 sequences, 32 kv heads, head_dim 64, q8_0 V)",
                        kernels=("kvq::k_attn_cols<64, 1>",),
