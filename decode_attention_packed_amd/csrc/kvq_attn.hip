@@ -1342,7 +1342,10 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
       first_tile = false;
     }
     if (t0 + kTile > app.lo && t0 < app.hi) patch_tile<D, VF>(ring + SL * S::BYTES, s_patch, t0, app);
-    process_tile<D, VF, DBG>(ring + SL * S::BYTES, t0, c1, t0 + kTile <= vis_lo, qa, dq, vis, st, dbg);
+    // (wave-uniform by construction; readfirstlane lets the compiler branch
+    // around the mask instead of masking lanes through it)
+    const bool full = __builtin_amdgcn_readfirstlane(t0 + kTile - vis_lo) <= 0;
+    process_tile<D, VF, DBG>(ring + SL * S::BYTES, t0, c1, full, qa, dq, vis, st, dbg);
   };
   run_ring<D, VF, SF>(p, seq, kvh, c1, ring_lds, tl, cur, tq, body);
   // a tile issued before the length was known and past it may still land
