@@ -59,14 +59,15 @@
 //    unpacked baseline page 1 compares against (A/B reference only, column
 //    layout and head_dim 128 only).  Its K tiles are twice as large, so that
 //    build runs 6 waves with 2 ring slots each.
-//  - kvq::w12 (kvq_attn_w12.hip): KVQ_COLS_Q4_128 builds only the column
-//    kernel for q4_0 V at head_dim 128, with 12 waves (3 per SIMD) and 2 ring
-//    slots each; the plain build hands those calls to it.
+//  - kvq::w12 (kvq_attn_w12.hip): KVQ_Q4_128_ONLY builds only the kernels
+//    for q4_0 V at head_dim 128 (both layouts, single calls and batched
+//    launches), with 12 waves (3 per SIMD) and 2 ring slots each; the plain
+//    build hands those calls to it when their chunks reach 1536 tokens.
 #ifndef KVQ_KFMT
 #define KVQ_KFMT 0
 #endif
-#ifndef KVQ_COLS_Q4_128
-#define KVQ_COLS_Q4_128 0
+#ifndef KVQ_Q4_128_ONLY
+#define KVQ_Q4_128_ONLY 0
 #endif
 
 namespace kvq {
@@ -434,9 +435,9 @@ __device__ __forceinline__ void wait_tiles(int pending) {
 //
 // The SIMDs issue their oldest wave first, so with an even deal the first
 // wave on each SIMD (waves 0-3) finishes well ahead of the others: by ~7 us
-// in the verify step's 128-tile chunks (row layout, 8 waves) and ~6 us in
-// the ragged batch (column layout, head_dim 64), leaving one wave per SIMD
-// for the rest of the chunk.  Those kernels therefore deal the last tiles
+// in 128-tile chunks of the 8-wave row layout (4 query tokens x 4 heads)
+// and ~6 us in the ragged batch (column layout, head_dim 64), leaving one
+// wave per SIMD for the rest of the chunk.  Those kernels therefore deal the last tiles
 // of a chunk of at least kSkewMin tiles round-robin to waves 0-3 only (a
 // fraction SF/64 of the chunk, at most a cap: kSkewF, kSkewCap), still a
 // fixed map: half of the row layout's chunk up to 32 tiles (the gap is
@@ -1932,7 +1933,7 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
                 const SplitPlan& plan, float sm_scale, int causal, void* workspace,
                 const float* k_new, const float* v_new, int n_new, hipStream_t stream,
                 int32_t* dbg_isum, int dbg_max_len, unsigned long long* dbg_stamps) {
-#if KVQ_KFMT == 0 && !KVQ_COLS_Q4_128
+#if KVQ_KFMT == 0 && !KVQ_Q4_128_ONLY
   // q4_0 V at head_dim 128 runs the 12-wave build when its chunks give
   // every wave at least 4 tiles
   if (c.head_dim == 128 && c.v_format == 0 && plan.chunk >= kW12MinChunk)
@@ -1946,7 +1947,7 @@ int launch_attn(const kvq_cache& c, const float* q, float* out, int n_seq, int n
   p.dbg_max_len = dbg_max_len;
   p.dbg_stamps = dbg_stamps;
   const dim3 grid((unsigned)((long long)p.n_groups_pad * plan.n_split));
-  if constexpr (KVQ_COLS_Q4_128) {
+  if constexpr (KVQ_Q4_128_ONLY) {
     if (c.head_dim != 128 || c.v_format != 0) return -4;   // not reached: only those calls come here
     launch_attn_kernel<128, 0>(p, grid, stream);
   } else if (c.head_dim == 128) {
@@ -2002,7 +2003,7 @@ int launch_attn_batch(const AttnCall* calls, const SplitPlan* plans, int n_calls
   }
   const kvq_cache& c = *calls[0].cache;
   const bool rows = b.p[0].rows * (c.head_dim / kBlock) > 16;
-#if KVQ_COLS_Q4_128
+#if KVQ_Q4_128_ONLY
   if (c.head_dim != 128 || c.v_format != 0) return -4;   // not reached: only those calls come here
   launch_batch_kernels<128, 0>(b, rows, stream);
 #else
