@@ -1109,15 +1109,20 @@ __device__ __forceinline__ float mul_f32_f16(float wq, uint32_t pair) {
 }
 
 // Running state of one wave: output tiles acc[n][i] = row l%16, dim
-// 16n + 4(l/16) + i; the running maximum of row l%16 and the sum of the
-// weights of this lane's tokens (the four lanes of a row are summed once, at
-// the end of the ring).
+// 16n + 4(l/16) + i; the reference of row l%16 (at least its running
+// maximum, log2 domain) and the sum of the weights of this lane's tokens
+// (the four lanes of a row are summed once, at the end of the ring).
 template <int D>
 struct WaveState {
   v4f acc[D / 16];
   float mrow;
   float lrow;
 };
+
+// Headroom of the row layout's softmax reference above a row's maximum
+// (log2 domain): right after a rescale the largest weight is
+// 2^(kPvShift - kRowHead), and scores up to kRowHead above it need none.
+constexpr float kRowHead = 2.0f;
 
 // One 32-token tile from its LDS slot: scores, online softmax update, P.V.
 // Both products run transposed, S^T = K Q^T and O^T += V^T P^T.  Score MFMA
@@ -1179,19 +1184,25 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, int t0, int c1, bool
     }
   }
 
-  // ---- online softmax: the row maximum over the tile, rescale when it grows
+  // ---- online softmax against a reference that only moves when a score
+  // passes it: then it goes kRowHead above the row's new maximum, and the
+  // row's sum and accumulators are rescaled.  With 16 rows and short chunks
+  // some row's maximum grows in most tiles; with the headroom a rescale is
+  // rare after a row's first tiles.  Every weight and sum stays relative to
+  // the same reference, so o / l and the split merge are unchanged, and no
+  // weight exceeds 2^kPvShift.
   float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                    fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-  mx = across32(across16(mx, fmax2), fmax2);
-  const float mnew = fmaxf(st.mrow, mx);
-  if (__any(mnew > st.mrow)) {
+  if (__any(mx > st.mrow)) {
+    mx = across32(across16(mx, fmax2), fmax2);   // the row maximum, in every lane of the row
+    const float mnew = mx > st.mrow ? mx + kRowHead : st.mrow;
     const float a = __builtin_amdgcn_exp2f(st.mrow - mnew);
     st.lrow *= a;
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) acc[n] *= a;
     st.mrow = mnew;
   }
-  const float mshift = st.mrow - kPvShift<VF>;   // the running maximum less the P.V shift
+  const float mshift = st.mrow - kPvShift<VF>;   // the reference less the P.V shift
   float pr[8];   // weights of row col, tokens t0 + 8*grp + j
 #pragma unroll
   for (int h = 0; h < 2; ++h)

@@ -61,3 +61,20 @@ def test_v_scale_verify_rows(scale):
         got = H.run_attention(cache, ci, table, max_segs)
         H.assert_close(got / scale, H.oracle_attention(ci) / scale,
                        f"verify {ci.spec.name} V x {scale:g}")
+
+
+@pytest.mark.parametrize("scale", [1e-2, 1e-3])
+def test_v_scale_rows_q8_0(scale):
+    """The row layout with q8_0 V (the smaller block scale, max|V| / 127) and
+    small V: 4 causal query tokens x 4 heads, 2 kv heads, 9000 tokens."""
+    rng = np.random.default_rng(4242)
+    L, hkv = 9000, 2
+    spec = W.CacheSpec("rows_q8", 1, 4, 4 * hkv, hkv, 128, L, W.V_Q8_0, causal=True)
+    ci = W.CacheInputs(spec, rng.standard_normal((1, 4, 4 * hkv, 128)).astype(np.float32),
+                       (rng.standard_normal((1, L, hkv, 128)) * 1.5).astype(np.float32),
+                       (rng.standard_normal((1, L, hkv, 128)) * scale).astype(np.float32),
+                       np.array([L], np.int32), None, 1, -(-L // 64) * 64)
+    print(f"[gpu-test] rows q8_0 V x {scale:g}", flush=True)
+    cache, table, max_segs = H.build_cache(ci)
+    got = H.run_attention(cache, ci, table, max_segs)
+    H.assert_close(got / scale, H.oracle_attention(ci) / scale, f"rows q8_0 V x {scale:g}")
