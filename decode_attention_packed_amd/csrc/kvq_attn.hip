@@ -25,9 +25,9 @@
 //          column scales its dots by d_q * d_k and a DPP butterfly over the
 //          block columns of a row adds them up: every lane then holds the
 //          scores of 8 consecutive tokens of one row, with no padding rows.
-//   softmax the running maximum is checked lane by lane; the cross-lane
-//          reduction and the rescale of the accumulators only run when a
-//          score exceeds it.
+//   softmax the row's reference (up to kRefHead above its running
+//          maximum) is checked lane by lane; the cross-lane reduction and
+//          the rescale of the accumulators only run when a score passes it.
 //   P.V    computed transposed, v_mfma_f32_16x16x32_f16 with A = 16 dims of
 //          V codes (exact fp16 integers from a byte permute and one packed
 //          f16 add) and B = p * d_v of the column's block rounded to fp16
@@ -891,6 +891,17 @@ __device__ __forceinline__ v8h bytes_to_f16x8(uint32_t w0, uint32_t w1, _Float16
 template <int VF>
 constexpr float kPvShift = VF == 0 ? 4.0f : 8.0f;
 
+// Headroom of the softmax reference above a row's maximum (log2 domain),
+// both layouts.  The reference only moves when a score passes it, and then
+// to kRefHead above the row's new maximum: right after such a rescale the
+// largest weight is 2^(kPvShift - kRefHead), and later scores up to
+// kRefHead higher need no rescale.  Every weight and sum of a row stays
+// relative to the same reference, so o / l and the split merge are
+// unchanged, and no weight exceeds 2^kPvShift.  A wave sees ~10-20 tiles
+// of a chunk, and without headroom some row's maximum grew in a third (4
+// rows) to most (16 rows) of them, each time rescaling every accumulator.
+constexpr float kRefHead = 2.0f;
+
 __device__ __forceinline__ uint32_t round_f16_pair(float p0, float p1, uint32_t dpair) {
   const v2h d = __builtin_bit_cast(v2h, dpair);
   const v2h r = {(_Float16)__builtin_fmaf(p0, (float)d.x, 0.0f), (_Float16)__builtin_fmaf(p1, (float)d.y, 0.0f)};
@@ -1119,11 +1130,6 @@ struct WaveState {
   float lrow;
 };
 
-// Headroom of the row layout's softmax reference above a row's maximum
-// (log2 domain): right after a rescale the largest weight is
-// 2^(kPvShift - kRowHead), and scores up to kRowHead above it need none.
-constexpr float kRowHead = 2.0f;
-
 // One 32-token tile from its LDS slot: scores, online softmax update, P.V.
 // Both products run transposed, S^T = K Q^T and O^T += V^T P^T.  Score MFMA
 // h takes token 8(m/4) + 4h + m%4 as its row m, so lane l receives the
@@ -1184,18 +1190,13 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, int t0, int c1, bool
     }
   }
 
-  // ---- online softmax against a reference that only moves when a score
-  // passes it: then it goes kRowHead above the row's new maximum, and the
-  // row's sum and accumulators are rescaled.  With 16 rows and short chunks
-  // some row's maximum grows in most tiles; with the headroom a rescale is
-  // rare after a row's first tiles.  Every weight and sum stays relative to
-  // the same reference, so o / l and the split merge are unchanged, and no
-  // weight exceeds 2^kPvShift.
+  // ---- online softmax against the row's reference (kRefHead): the row
+  // maximum and the rescale only when a score passes it
   float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
                    fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
   if (__any(mx > st.mrow)) {
     mx = across32(across16(mx, fmax2), fmax2);   // the row maximum, in every lane of the row
-    const float mnew = mx > st.mrow ? mx + kRowHead : st.mrow;
+    const float mnew = mx > st.mrow ? mx + kRefHead : st.mrow;
     const float a = __builtin_amdgcn_exp2f(st.mrow - mnew);
     st.lrow *= a;
 #pragma unroll
@@ -1399,10 +1400,11 @@ __device__ __forceinline__ void attn_rows_body(const AttnParams& p, int blk) {
 // ---------------------------------------------------------------------------
 
 // Per-lane state: acc[g][i] = sum over tokens of p * V for dim 16g + 4*(l/16)
-// + i of this lane's column; m is the row's running maximum (log2 domain),
-// c0 = kPvShift - m on the block-0 lane of a live row (so the block sum
-// yields score - m + kPvShift) and -1e30 on the block-0 lane of a padding
-// column; l sums this lane's weights (each 2^kPvShift times p).
+// + i of this lane's column; m is the row's softmax reference (at least its
+// running maximum, log2 domain; kRefHead), c0 = kPvShift - m on the block-0
+// lane of a live row (so the block sum yields score - m + kPvShift) and
+// -1e30 on the block-0 lane of a padding column; l sums this lane's weights
+// (each 2^kPvShift times p).
 template <int D>
 struct ColState {
   v4f acc[D / 16];
@@ -1507,10 +1509,12 @@ __device__ __forceinline__ void process_tile_cols(const uint8_t* slot, int t0, i
     // row maximum over the four lane groups (the block lanes agree already)
     const float rm = across32(across16(mx, fmax2), fmax2);
     float delta;
+    // the reference moves kRefHead above the new maximum of the rows that
+    // passed it
     if (first) {
-      delta = rm == -INFINITY ? 0.0f : rm - kShift;   // nothing accumulated yet
+      delta = rm == -INFINITY ? 0.0f : rm - kShift + kRefHead;   // nothing accumulated yet
     } else {
-      delta = fmaxf(rm - kShift, 0.0f);
+      delta = rm > kShift ? rm - kShift + kRefHead : 0.0f;
       const float a = __builtin_amdgcn_exp2f(-delta);
 #pragma unroll
       for (int g = 0; g < NG; ++g) st.acc[g] *= a;
