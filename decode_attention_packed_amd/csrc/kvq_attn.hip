@@ -1185,8 +1185,10 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, int t0, int c1, bool
       for (int i = 0; i < 4; ++i) s[h][i] = fmaf((float)c[i], w[i], s[h][i]);
     }
     if (!full) {
+      const int lim = vis - t0 - 8 * grp - 4 * h;   // tokens i >= lim are not visible to row col
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s[h][i] = t0 + 8 * grp + 4 * h + i < vis ? s[h][i] : -INFINITY;
+      for (int i = 0; i < 4; ++i)
+        if (i >= lim) s[h][i] = -INFINITY;
     }
   }
 
@@ -1220,9 +1222,10 @@ __device__ __forceinline__ void process_tile(uint8_t* slot, int t0, int c1, bool
     dv[b] = *reinterpret_cast<const v8h*>(slot + S::DV_OFF + b * 64 + 16 * grp);
   if (t0 + kTile > c1) {
     // tokens past the chunk end may hold anything (even non-finite scales)
+    const int lim = c1 - t0 - 8 * grp;   // tokens j >= lim are past it
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (t0 + 8 * grp + j >= c1) {
+      if (j >= lim) {
 #pragma unroll
         for (int b = 0; b < NB; ++b) dv[b][j] = (_Float16)0.0f;
       }
