@@ -5,7 +5,9 @@ chunks reach 1536 tokens (12 waves x 4 tiles), in a single call and in a
 batched launch.  Every case is checked against the oracle on all query
 heads; the per-block int32 sums of the 12-wave row kernel are compared bit
 for bit.  Chunk sizes are forced through KVQ_CHUNK_TOKENS, so the lengths
-below end in short last splits and partial tiles."""
+below end in short last splits and partial tiles; ragged sequences in
+shuffled append-only segments (page 3, "BitLLM", how it differs) and calls
+without a segment table take the same kernels."""
 import numpy as np
 import pytest
 
@@ -86,3 +88,55 @@ def test_w12_rows_batched_verify():
     outs, _ = run_batch(cis)
     for ci, got in zip(cis, outs):
         H.assert_close(got, H.oracle_attention(ci), "w12 batched verify " + ci.spec.name)
+
+
+def _ragged_segmented(lens, seg, tq, g, hkv, seed):
+    """Sequences of the given lengths in `seg`-token segments, dealt from a
+    shuffled pool (the segment table of the ragged recipe)."""
+    rng = np.random.default_rng(seed)
+    lens = np.asarray(lens, np.int32)
+    spec = W.CacheSpec("w12rows_seg", len(lens), tq, g * hkv, hkv, 128, int(lens.max()), W.V_Q4_0,
+                       causal=True)
+    q = rng.standard_normal((len(lens), tq, g * hkv, 128)).astype(np.float32)
+    k = [(rng.standard_normal((int(n), hkv, 128)) * 1.5).astype(np.float32) for n in lens]
+    v = [rng.standard_normal((int(n), hkv, 128)).astype(np.float32) for n in lens]
+    nseg = (lens + seg - 1) // seg
+    pool = rng.permutation(int(nseg.sum())).astype(np.int32)
+    table = np.full((len(lens), int(nseg.max())), -1, np.int32)
+    pos = 0
+    for i, n in enumerate(nseg):
+        table[i, :n] = pool[pos:pos + n]
+        pos += n
+    return W.CacheInputs(spec, q, k, v, lens, table, int(nseg.sum()), seg)
+
+
+def test_w12_rows_ragged_segments(monkeypatch):
+    """Three sequences of 9000, 2500 and 6001 tokens in shuffled 1024-token
+    segments, 1536-token chunks: splits cross segment boundaries, the short
+    sequence's work-groups leave early, and the fused append lands in each
+    sequence's last segment."""
+    monkeypatch.setenv("KVQ_CHUNK_TOKENS", "1536")
+    ci = _ragged_segmented([9000, 2500, 6001], 1024, 4, 4, 2, seed=515)
+    _say("w12 rows ragged segments")
+    cache, table, max_segs = H.build_cache(ci)
+    want = H.oracle_attention(ci)
+    H.assert_close(H.run_attention(cache, ci, table, max_segs), want, "w12 rows ragged segments")
+    del cache
+    got, cache = run_fused(ci, 4)
+    check_appended_rows(cache, ci, 4)
+    H.assert_close(got, want, "w12 rows ragged segments fused")
+
+
+def test_w12_rows_no_table(monkeypatch):
+    """The contiguous form without a segment table (sequence i owns segments
+    i*max_segs ..): tiles go out before the length is known, bounded by
+    max_seq_len, so the shorter sequence's work-groups load past its end."""
+    monkeypatch.setenv("KVQ_CHUNK_TOKENS", "1536")
+    from tests.test_gpu_no_table import _attend, _build, _inputs as nt_inputs
+    ci = nt_inputs([7000, 3100], 2, 4, 4, 128, W.V_Q4_0, True, seed=616)
+    _say("w12 rows without a table")
+    cache = _build(ci)
+    H.assert_close(_attend(cache, ci), H.oracle_attention(ci), "w12 rows no table")
+    cache = _build(ci, skip_last=4)
+    got = _attend(cache, ci, append_rows=4)
+    H.assert_close(got, H.oracle_attention(ci), "w12 rows no table fused")
