@@ -1135,9 +1135,10 @@ struct WaveState {
 // h takes token 8(m/4) + 4h + m%4 as its row m, so lane l receives the
 // scores of row l%16 for tokens 8(l/16) + 4h + i: over h and i, the 8 tokens
 // 8(l/16) .. +8, which is the k-range of lane l's B operand in the P.V MFMA.
-// P thus stays in registers, and the row maximum is an in-lane max plus two
-// exchanges between the lanes of a row.  `full`: every token of the tile is
-// visible to every query row (no mask).
+// P thus stays in registers, and the softmax check is an in-lane maximum
+// against the row's reference (kRefHead), with the two exchanges between
+// the lanes of a row only when a score passes it.  `full`: every token of
+// the tile is visible to every query row (no mask).
 template <int D, int VF, int DBG = 0>
 __device__ __forceinline__ void process_tile(uint8_t* slot, int t0, int c1, bool full,
                                              const long (&qa)[D / kBlock], const float (&dq)[D / kBlock],
