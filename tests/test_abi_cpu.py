@@ -243,6 +243,38 @@ def test_batch_args_rejected():
     assert run([call(c128), call(c128, hq=16)], ws_bytes=two - 16) == K.KVQ_ERR_WORKSPACE
 
 
+def _ws_bytes(c, n_seq, n_qtok, hq, splits):
+    """Workspace bytes of one call under a given split count (256-byte
+    counters, then the partial rows, then their (m, l), each part rounded)."""
+    groups = n_seq * c.n_kv_heads
+    rows = n_qtok * (hq // c.n_kv_heads)
+    return (_r256(groups * 256) + _r256(groups * splits * rows * c.head_dim * 4)
+            + _r256(groups * splits * rows * 8))
+
+
+@pytest.mark.parametrize("max_len,splits", [
+    (131072, 21),   # the verify step: 21 splits of 6272 tokens (252 work-groups), not 20 + a short one
+    (40000, 21),    # 1920-token chunks: long enough for the 12-wave kernels (1536 and up)
+    (3000, 12),     # short caches: 256-token chunks
+])
+def test_batch_joint_plan(max_len, splits):
+    """The joint split plan of a batched launch with fewer than 256 groups:
+    one chunk for both calls of the verify step (main 32/8 heads and draft
+    16/4, 4 causal query tokens), the shortest whole number of tiles that
+    keeps the grid within 256 work-groups, pinned through the batch's
+    workspace size (host only)."""
+    main = _fake_cache(n_kv_heads=8, seg_tokens=(max_len + 63) // 64 * 64)
+    draft = _fake_cache(n_kv_heads=4, seg_tokens=(max_len + 63) // 64 * 64)
+
+    def call(cache, hq):
+        return K._lib.KvqAttnCallStruct(ctypes.pointer(cache), 0x5000, 0x6000, 1, 4, hq, None, 1,
+                                        0x7000, max_len, 0.1, 1)
+    arr = (K._lib.KvqAttnCallStruct * 2)(call(main, 32), call(draft, 16))
+    n = ctypes.c_size_t(0)
+    assert K.lib().attn_decode_packed_batch_workspace_size(arr, 2, ctypes.byref(n)) == K.KVQ_OK
+    assert n.value == _ws_bytes(main, 1, 4, 32, splits) + _ws_bytes(draft, 1, 4, 16, splits)
+
+
 def _noalloc(c, q=0x5000, out=0x6000, n_seq=1, n_qtok=1, hq=32, table=None, max_segs=1,
              seq_len=0x7000, max_len=1024, scale=0.1):
     return K.lib().attn_decode_packed_noalloc(ctypes.byref(c), q, out, n_seq, n_qtok, hq, table,
