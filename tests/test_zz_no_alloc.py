@@ -47,11 +47,12 @@ def _run(c, noalloc):
 
 
 def test_noalloc_matches_workspace_entry_point():
+    rows_big = _case(W.make_inputs("verify128k", ctx=65536)[0])   # 12-wave row kernels + merge launch
     big = _case(W.make_inputs("long128k", ctx=65536)[0])        # 12-wave build, 32 splits
     small = _case(W.make_inputs("gqa8k", ctx=4096)[0])          # 8-wave build, 16 splits
     rows = _case(W.make_inputs("verify128k", ctx=3000)[1])      # row layout + merge launch
-    for name, c in (("65536 tokens", big), ("gqa8k 4096", small), ("verify draft 3000", rows),
-                    ("65536 tokens again", big)):
+    for name, c in (("verify main 65536", rows_big), ("65536 tokens", big), ("gqa8k 4096", small),
+                    ("verify draft 3000", rows), ("verify main 65536 again", rows_big)):
         print(f"[gpu-test] noalloc {name}", flush=True)
         got = _run(c, noalloc=True)
         want = _run(c, noalloc=False)
