@@ -236,7 +236,8 @@ def test_attention_shapes_and_ragged_tails(D, G, fmt, L):
                                                 (128, 16, 1, True, 130, 0), (128, 3, 4, False, 4100, 1),
                                                 (128, 4, 2, True, 4, 0), (128, 5, 3, True, 700, 1),
                                                 (64, 4, 4, True, 1500, 1), (64, 16, 1, True, 300, 0),
-                                                (64, 3, 4, False, 2100, 0), (64, 9, 1, True, 9, 1)])
+                                                (64, 3, 4, False, 2100, 0), (64, 9, 1, True, 9, 1),
+                                                (128, 1, 16, False, 3000, 0), (64, 1, 16, True, 777, 1)])
 def test_attention_multi_query(D, Tq, G, causal, L, fmt):
     """The row layout (more than 16 query-row x block columns): head_dim 128
     and 64, both V formats, causal and not, contexts down to the query count."""
