@@ -41,9 +41,10 @@ def _inputs(L, tq, g, hkv, seed):
 
 # (L, chunk, query tokens, heads per kv head): 16 rows; 12 rows (4 padding
 # rows in the MFMA columns); 16 query tokens of one head each; one query
-# token of 16 grouped heads
+# token of 16 grouped heads; a last split of one token, which only the last
+# query token sees (the other rows' partials of that split are empty)
 CASES = [(6001, 1536, 4, 4), (8191, 2048, 4, 4), (5000, 1536, 3, 4), (7001, 1536, 16, 1),
-         (9000, 2048, 1, 16)]
+         (9000, 2048, 1, 16), (6145, 1536, 4, 4)]
 
 
 @pytest.mark.parametrize("L,chunk,tq,g", CASES)
