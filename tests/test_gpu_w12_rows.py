@@ -143,3 +143,18 @@ def test_w12_rows_no_table(monkeypatch):
     cache = _build(ci, skip_last=4)
     got = _attend(cache, ci, append_rows=4)
     H.assert_close(got, H.oracle_attention(ci), "w12 rows no table fused")
+
+
+def test_w12_rows_batched_mixed_calls():
+    """Three row-layout calls of different kv-head counts and lengths in one
+    batched launch (40000 tokens at 32/8 heads, 30000 at 16/4, 20000 at
+    8/2; 4 causal query tokens each): the joint plan's 1920-token chunks run
+    the 12-wave batch kernels with 21, 16 and 11 splits, and the merge
+    launch combines each call's own split count.  All heads of every call
+    against the oracle."""
+    cis = [_inputs(40000, 4, 4, 8, seed=41), _inputs(30000, 4, 4, 4, seed=42),
+           _inputs(20000, 4, 4, 2, seed=43)]
+    _say("w12 rows batched, three calls")
+    outs, _ = run_batch(cis)
+    for i, (ci, got) in enumerate(zip(cis, outs)):
+        H.assert_close(got, H.oracle_attention(ci), f"w12 batched call {i}")
